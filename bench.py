@@ -1,0 +1,182 @@
+"""Benchmark of the Lightning Attention chunked prefill on one MI355X.
+
+One step = one la_prefill_fwd call over the whole workload: B=2, T=8192, H=HV=64, D=DV=128, bf16 Q/K/V/O,
+FP32 state read from and written back to a 2-slot pool in place (every step sees the previous step's state;
+the work per step is identical). Inputs are synthetic (la_synth recipe, seed 1) and resident in HBM before the
+timed region. Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--config {0,1,2,3,4}]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LA prefill Mtok·head/s and % MFMA/HBM roofline at B=2,T=8192,H=64,D=128"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2516.6    # MI355X dense bf16 matrix peak
+CHUNK = 64
+
+
+def algorithmic_bytes(w):
+    """Bytes the path must move at minimum: q, k read once per q/k head, v read and o written once per value
+    head (bf16), plus the FP32 state read (READ) and written (WRITE) once per selected (sequence, head)."""
+    tok = w.tokens
+    qk = 2 * tok * w.H * 128 * 2
+    vo = 2 * tok * w.HV * 128 * 2
+    nstate = 0
+    if w.state_idx is not None and w.pool is not None:
+        P = w.pool.shape[0]
+        nsel = sum(1 for s in w.state_idx if 0 <= int(s) < P)
+        nstate = nsel * w.HV * 128 * 128 * 4 * ((w.flags & 1) + ((w.flags >> 1) & 1))
+    return qk + vo + nstate
+
+
+def mfma_flops_executed(w):
+    """Dense bf16 MFMA flops the kernel issues per call: per 64-token chunk and value head, scores 64x64x128 (by
+    both workgroups of a head), P.V 64x128x64 (block lower triangle, P as hi+lo), Q.S^T 64x128x128 (S as hi+lo),
+    state update 128x128x64 (V_dec as hi+lo), plus the identity transposes."""
+    per_chunk_head = (
+        2 * (10 / 16) * 64 * 64 * 128 * 2        # scores: 10 of 16 tiles, computed in each of the 2 value halves
+        + 2 * (12 / 16) * 64 * 128 * 64 * 2     # P.V: 6 of 8 32-token blocks per column tile, hi + lo
+        + 2 * 64 * 128 * 128 * 2                # Q.S^T with S hi + lo
+        + 2 * 128 * 128 * 64 * 2                # state update with V_dec hi + lo
+        + 2 * (32 + 8) * 16 * 16 * 16 * 2       # identity transposes of K (both halves) and V
+    )
+    chunks = sum((l + CHUNK - 1) // CHUNK for _, l in w.seq_rows())
+    return per_chunk_head * chunks * w.HV
+
+
+def cpu_baseline(w, max_units=None):
+    """Time the FP64 oracle on a bounded sample of the same workload: whole (sequence, value head) units."""
+    import numpy as np
+    import oracle
+    th = oracle.threads()
+    n_units = max_units or 128
+    rows = w.seq_rows()
+    units = []
+    for hv in range(w.HV):
+        for n in range(w.nseq):
+            units.append((rows[n][0], rows[n][1], hv))
+    units = units[:n_units]
+    q = w.q.reshape(-1, w.H, 128)
+    k = w.k.reshape(-1, w.H, 128)
+    v = w.v.reshape(-1, w.HV, 128)
+    oracle.tokenwise(q, k, v, w.H, w.HV, w.scale, w.slope, units[:1])       # warm
+    t0 = time.perf_counter()
+    oracle.tokenwise(q, k, v, w.H, w.HV, w.scale, w.slope, units)
+    dt = time.perf_counter() - t0
+    tokheads = sum(u[1] for u in units)
+    return {"value": tokheads / dt / 1e6, "unit": "Mtok·head/s", "cores": th, "kind": "oracle",
+            "sample": f"{len(units)} whole (sequence, value head) units of {rows[0][1]} tokens each "
+                      f"({tokheads} tok·head), FP64 tokenwise recurrence, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
+              f"multi-GPU sharding in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import la_synth
+    import linear_attention_decay_amd as la
+
+    w = la_synth.config(args.config)
+    dev = torch.device("cuda:0")
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q = to_dev(w.q).view(torch.bfloat16)
+    k = to_dev(w.k).view(torch.bfloat16)
+    v = to_dev(w.v).view(torch.bfloat16)
+    o = torch.empty_like(v)
+    slope = to_dev(w.slope)
+    pool = None if w.pool is None else to_dev(w.pool)
+    idx = None if w.state_idx is None else to_dev(w.state_idx)
+    cu = None if w.cu_seqlens is None else to_dev(w.cu_seqlens)
+    flags = w.flags
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        if cu is None:
+            la.la_prefill_fwd(q, k, v, o, slope, scale=w.scale, state_pool=pool, state_idx=idx, flags=flags,
+                              stream=stream)
+        else:
+            la.la_prefill_fwd_varlen(q, k, v, o, cu, slope, scale=w.scale, state_pool=pool, state_idx=idx,
+                                     flags=flags, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back launches on the launch stream, bracketed by events on that stream
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / args.steps
+
+    # per-launch kernel durations (events around each launch on the same stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    kern_ms = sum(per) / len(per)
+
+    tokheads = w.tokens * w.HV
+    value = tokheads / (ms_per_step * 1e-3) / 1e6
+    alg_bytes = algorithmic_bytes(w)
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    mfma_tfs = mfma_flops_executed(w) / (kern_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "Mtok·head/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "HV": w.HV, "D": 128, "DV": 128,
+                   "chunk": CHUNK, "state_flags": w.flags, "tokens": w.tokens},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "la_chunk_kernel<0>", "kernel_ms_avg": round(kern_ms, 6),
+                     "kernel_ms_median": round(per[len(per) // 2], 6), "algorithmic_bytes": alg_bytes},
+        "mfma": {"executed_tflops": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                 "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)},
+    }
+    if not args.no_cpu_baseline and args.config in (0, 1):
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,119 @@
+/*
+ * la_prefill.h -- C ABI of the Lightning Attention chunked prefill library for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "[LA] Lightning Attention MTP decode + KVBuffer parallel verify / commit", Description,
+ * the closed form used by verify; page "[Lightning Attention] Add Hopper SM90 CuTe DSL prefill", Description
+ * and Reviewer notes): for every sequence and value head hv, with q/k head h = hv / (HV / H) and
+ * lambda = exp(-slope[hv]),
+ *
+ *     S_t = lambda * S_{t-1} + v_t k_t^T,     o_t = scale * S_t q_t,     S_{-1} = S0 (or 0),
+ *
+ * i.e. o_t = scale * (lambda^{t+1} S0 q_t + sum_{i<=t} lambda^{t-i} (q_t . k_i) v_i). S is FP32, DV x D = 128 x 128,
+ * in [V, K] orientation (row = value index, column = key index). The library evaluates it in 64-token chunks on
+ * bf16 matrix cores with FP32 accumulation; the FP32 state stays on chip across a sequence's chunks.
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library never allocates, frees or
+ *     synchronises, and never reads device memory from the host. All work is enqueued on `stream`, which is
+ *     passed to the runtime verbatim (0 is the null stream).
+ *   - Tensors are dense and row-major with the last dimension fastest:
+ *       q, k  : bf16 [tokens, H, 128]        v, o : bf16 [tokens, HV, 128]
+ *       state pool : fp32 [pool_size, HV, 128 (V), 128 (K)]      slope : fp32 [HV]
+ *     Fixed-length calls index tokens as b * T + t. Pointers must be 16-byte aligned.
+ *   - State pool: sequence n uses slot state_idx[n]. A slot < 0 or >= pool_size means "no state": the
+ *     sequence starts from zero and its final state is not stored. With LA_STATE_READ the initial state is
+ *     read from the slot; with LA_STATE_WRITE the final state is stored into the same slot (in place).
+ *     Slots no sequence selects are never touched. Two sequences selecting the same slot with
+ *     LA_STATE_WRITE is undefined. state_pool / state_idx may be NULL only when flags == 0.
+ *   - o is written for every valid token (nothing relies on o being pre-initialised).
+ *   - Device values (slot indices, cu_seqlens, accepted lengths) are not validated and cost no host sync;
+ *     out-of-range values are clamped or skipped on the device as documented per call, never dereferenced
+ *     out of bounds. Slopes must be >= 0 (+inf is allowed and means lambda = 0).
+ *   - Host-checkable problems return an error before anything is enqueued:
+ *       D != 128, DV != 128, H <= 0, HV % H != 0            -> LA_ERR_UNSUPPORTED
+ *       negative sizes, NULL required pointer, bad flags     -> LA_ERR_INVALID_ARG
+ *     A call with no tokens and no sequences is a successful no-op. A launch failure returns LA_ERR_HIP.
+ *     la_last_error() then describes the failure (thread-local).
+ */
+#ifndef LA_PREFILL_H
+#define LA_PREFILL_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_ABI_VERSION 1
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARG = 1,
+    LA_ERR_UNSUPPORTED = 2,
+    LA_ERR_HIP = 3
+} la_status;
+
+/* flags bitmask */
+enum { LA_STATE_READ = 1u, LA_STATE_WRITE = 2u };
+
+/* packed-sequence scheduling */
+enum { LA_SCHED_AUTO = 0, LA_SCHED_PERSISTENT = 1, LA_SCHED_NONPERSISTENT = 2 };
+
+/*
+ * Fixed-length batched prefill (prefill page, Description: fixed-length BF16 prefill, optional initial/final
+ * state, MHA and GVA, explicit state-pool indices).
+ *   q, k        : bf16 [B, T, H, 128];  v, o : bf16 [B, T, HV, 128]
+ *   scale       : multiplies both the history term and the within-sequence term
+ *   state_idx   : int32 [B] (device)
+ * B == 0 or T == 0 is a no-op except that, with T == 0 and LA_STATE_WRITE, each selected slot receives its
+ * initial state (S0 with LA_STATE_READ, else zeros).
+ */
+la_status la_prefill_fwd(const void *q, const void *k, const void *v, void *o, int32_t B, int32_t T, int32_t H,
+                         int32_t HV, int32_t D, int32_t DV, float scale, const float *slope, float *state_pool,
+                         int32_t pool_size, const int32_t *state_idx, uint32_t flags, hipStream_t stream);
+
+/*
+ * Packed variable-length prefill (prefill page, Description: packed variable-length BF16 prefill; persistent
+ * or non-persistent packed scheduling). Sequence n occupies token rows [cu_seqlens[n], cu_seqlens[n+1]);
+ * chunks never straddle sequences.
+ *   q, k        : bf16 [total_T, H, 128];  v, o : bf16 [total_T, HV, 128]
+ *   cu_seqlens  : int32 [N + 1] (device), cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N] = total_T.
+ *                 Values are clamped into [0, total_T] on the device.
+ *   state_idx   : int32 [N] (device)
+ *   schedule    : LA_SCHED_* ; every schedule produces bitwise identical o and states.
+ * A zero-length sequence writes no output; with LA_STATE_WRITE its slot receives its initial state.
+ */
+la_status la_prefill_fwd_varlen(const void *q, const void *k, const void *v, void *o, const int32_t *cu_seqlens,
+                                int32_t N, int32_t total_T, int32_t H, int32_t HV, int32_t D, int32_t DV,
+                                float scale, const float *slope, float *state_pool, int32_t pool_size,
+                                const int32_t *state_idx, uint32_t flags, int32_t schedule, hipStream_t stream);
+
+/*
+ * Commit after a short-chunk verify (verify page, Description: state-update advances the pooled state by the
+ * per-request accepted prefix length L and skips padded slots; Tests: L = 0 is a no-op):
+ *     S <- lambda^L S + sum_{i<L} lambda^{L-1-i} v_i k_i^T   over request b's first L tokens.
+ *   k           : bf16 [B, T, H, 128];  v : bf16 [B, T, HV, 128]
+ *   state_idx   : int32 [B] (device); slot < 0 or >= pool_size: request skipped
+ *   accepted_len: int32 [B] (device), 0 <= L <= T (clamped into that range on the device)
+ * L == 0 leaves the slot bitwise unchanged. The verify outputs themselves come from la_prefill_fwd with
+ * flags = LA_STATE_READ on the same T draft tokens.
+ */
+la_status la_state_commit(const void *k, const void *v, int32_t B, int32_t T, int32_t H, int32_t HV, int32_t D,
+                          int32_t DV, const float *slope, float *state_pool, int32_t pool_size,
+                          const int32_t *state_idx, const int32_t *accepted_len, hipStream_t stream);
+
+/* Static name of a status code. */
+const char *la_status_string(la_status s);
+
+/* Thread-local description of the last non-OK status returned on this thread ("" if none). */
+const char *la_last_error(void);
+
+/* LA_ABI_VERSION of the built library. */
+int32_t la_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_PREFILL_H */

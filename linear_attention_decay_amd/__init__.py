@@ -1,0 +1,22 @@
+"""Lightning Attention chunked prefill on AMD Instinct MI355X (gfx950).
+
+The computation lives in liblaprefill.so (C ABI: include/la_prefill.h); this package is its Python binding.
+Importing it fails loudly when the library has not been built.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LA_ERR_HIP,
+    LA_ERR_INVALID_ARG,
+    LA_ERR_UNSUPPORTED,
+    LA_OK,
+    LA_SCHED_AUTO,
+    LA_SCHED_NONPERSISTENT,
+    LA_SCHED_PERSISTENT,
+    LA_STATE_READ,
+    LA_STATE_WRITE,
+    LaError,
+    la_prefill_fwd,
+    la_prefill_fwd_varlen,
+    la_state_commit,
+    lib,
+)

@@ -1,0 +1,135 @@
+"""Thin ctypes binding of liblaprefill.so (include/la_prefill.h). Argument marshalling only.
+
+Device memory and streams come from torch; every step of the computation runs in the library's HIP kernels.
+The functions have the same names as the C entry points and derive the sizes from the tensor shapes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liblaprefill.so")
+
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
+LA_STATE_READ, LA_STATE_WRITE = 1, 2
+LA_SCHED_AUTO, LA_SCHED_PERSISTENT, LA_SCHED_NONPERSISTENT = 0, 1, 2
+
+EXPORTS = ("la_prefill_fwd", "la_prefill_fwd_varlen", "la_state_commit", "la_status_string", "la_last_error",
+           "la_abi_version")
+
+
+class LaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"HIP library not built: {LIB_PATH} is missing; run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i32, u32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float
+    L.la_prefill_fwd.restype = ctypes.c_int
+    L.la_prefill_fwd.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, u32, p]
+    L.la_prefill_fwd_varlen.restype = ctypes.c_int
+    L.la_prefill_fwd_varlen.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, u32, i32, p]
+    L.la_state_commit.restype = ctypes.c_int
+    L.la_state_commit.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p, p, i32, p, p, p]
+    L.la_status_string.restype = ctypes.c_char_p
+    L.la_status_string.argtypes = [ctypes.c_int]
+    L.la_last_error.restype = ctypes.c_char_p
+    L.la_last_error.argtypes = []
+    L.la_abi_version.restype = i32
+    L.la_abi_version.argtypes = []
+    return L
+
+
+lib = _load()
+
+
+def _check(status):
+    if status != LA_OK:
+        raise LaError(status, f"{lib.la_status_string(status).decode()}: {lib.la_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, dev):
+    import torch
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _req(t, name, dtype, dev):
+    import torch
+    if t is None:
+        return
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} must live on {dev}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def la_prefill_fwd(q, k, v, o, slope, scale=1.0, state_pool=None, state_idx=None, flags=0, stream=None):
+    """Fixed-length prefill. q, k: bf16 [B, T, H, 128]; v, o: bf16 [B, T, HV, 128]; slope: fp32 [HV];
+    state_pool: fp32 [P, HV, 128, 128]; state_idx: int32 [B]; flags: LA_STATE_READ | LA_STATE_WRITE."""
+    import torch
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _req(t, n, torch.bfloat16, dev)
+    _req(slope, "slope", torch.float32, dev)
+    _req(state_pool, "state_pool", torch.float32, dev)
+    _req(state_idx, "state_idx", torch.int32, dev)
+    B, T, H, D = q.shape
+    HV, DV = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T) or o.shape != v.shape:
+        raise ValueError("shape mismatch between q, k, v, o")
+    P = 0 if state_pool is None else state_pool.shape[0]
+    _check(lib.la_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, HV, D, DV, float(scale), _ptr(slope),
+                              _ptr(state_pool), P, _ptr(state_idx), int(flags), _stream(stream, dev)))
+    return o
+
+
+def la_prefill_fwd_varlen(q, k, v, o, cu_seqlens, slope, scale=1.0, state_pool=None, state_idx=None, flags=0,
+                          schedule=LA_SCHED_AUTO, stream=None):
+    """Packed prefill. q, k: bf16 [total_T, H, 128]; v, o: bf16 [total_T, HV, 128]; cu_seqlens: int32 [N+1]."""
+    import torch
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _req(t, n, torch.bfloat16, dev)
+    _req(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _req(slope, "slope", torch.float32, dev)
+    _req(state_pool, "state_pool", torch.float32, dev)
+    _req(state_idx, "state_idx", torch.int32, dev)
+    total_T, H, D = q.shape
+    HV, DV = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != total_T or o.shape != v.shape:
+        raise ValueError("shape mismatch between q, k, v, o")
+    N = cu_seqlens.shape[0] - 1
+    P = 0 if state_pool is None else state_pool.shape[0]
+    _check(lib.la_prefill_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens), N, total_T, H, HV, D, DV,
+                                     float(scale), _ptr(slope), _ptr(state_pool), P, _ptr(state_idx), int(flags),
+                                     int(schedule), _stream(stream, dev)))
+    return o
+
+
+def la_state_commit(k, v, slope, state_pool, state_idx, accepted_len, stream=None):
+    """Commit accepted draft tokens: k: bf16 [B, T, H, 128]; v: bf16 [B, T, HV, 128]; accepted_len: int32 [B]."""
+    import torch
+    dev = k.device
+    _req(k, "k", torch.bfloat16, dev)
+    _req(v, "v", torch.bfloat16, dev)
+    _req(slope, "slope", torch.float32, dev)
+    _req(state_pool, "state_pool", torch.float32, dev)
+    _req(state_idx, "state_idx", torch.int32, dev)
+    _req(accepted_len, "accepted_len", torch.int32, dev)
+    B, T, H, D = k.shape
+    HV, DV = v.shape[2], v.shape[3]
+    _check(lib.la_state_commit(_ptr(k), _ptr(v), B, T, H, HV, D, DV, _ptr(slope), _ptr(state_pool),
+                               state_pool.shape[0], _ptr(state_idx), _ptr(accepted_len), _stream(stream, dev)))
+    return state_pool

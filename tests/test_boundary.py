@@ -1,0 +1,95 @@
+"""Host-side checks of the C-ABI library (no GPU): it loads, exports every declared symbol, and rejects
+host-checkable problems before enqueuing anything (prefill page, Description: unsupported specialisations
+fail explicitly rather than silently falling back)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la_prefill.h")
+
+la = pytest.importorskip("linear_attention_decay_amd")
+L = la.lib
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below returns before any launch
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) == set(la.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert L.la_abi_version() == 1
+    assert L.la_status_string(0) == b"LA_OK"
+    assert L.la_status_string(2) == b"LA_ERR_UNSUPPORTED"
+
+
+def _fwd(B=1, T=64, H=2, HV=2, D=128, DV=128, slope=FAKE, pool=None, P=0, idx=None, flags=0, q=FAKE):
+    return L.la_prefill_fwd(q, FAKE, FAKE, FAKE, B, T, H, HV, D, DV, 1.0, slope, pool, P, idx, flags, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), la.LA_ERR_UNSUPPORTED),
+    (dict(DV=256), la.LA_ERR_UNSUPPORTED),
+    (dict(H=3, HV=4), la.LA_ERR_UNSUPPORTED),
+    (dict(H=4, HV=2), la.LA_ERR_UNSUPPORTED),
+    (dict(H=0, HV=0), la.LA_ERR_UNSUPPORTED),
+    (dict(B=-1), la.LA_ERR_INVALID_ARG),
+    (dict(T=-5), la.LA_ERR_INVALID_ARG),
+    (dict(slope=None), la.LA_ERR_INVALID_ARG),
+    (dict(flags=1), la.LA_ERR_INVALID_ARG),                       # READ without pool / idx
+    (dict(flags=2, pool=FAKE, P=1), la.LA_ERR_INVALID_ARG),       # WRITE without idx
+    (dict(flags=4, pool=FAKE, P=1, idx=FAKE), la.LA_ERR_INVALID_ARG),
+    (dict(q=None), la.LA_ERR_INVALID_ARG),
+    (dict(flags=3, pool=FAKE, P=-1, idx=FAKE), la.LA_ERR_INVALID_ARG),
+])
+def test_fixed_rejects_before_launch(kw, status):
+    assert _fwd(**kw) == status
+    assert L.la_last_error() != b""
+
+
+def test_empty_calls_are_noops():
+    assert _fwd(B=0) == la.LA_OK
+    assert _fwd(T=0) == la.LA_OK
+    assert L.la_last_error() == b""
+    assert L.la_prefill_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 2, 2, 128, 128, 1.0, FAKE, None, 0, None, 0,
+                                   0, None) == la.LA_OK
+    assert L.la_state_commit(FAKE, FAKE, 0, 8, 2, 2, 128, 128, FAKE, FAKE, 4, FAKE, FAKE, None) == la.LA_OK
+    assert L.la_state_commit(FAKE, FAKE, 4, 0, 2, 2, 128, 128, FAKE, FAKE, 4, FAKE, FAKE, None) == la.LA_OK
+
+
+def test_varlen_rejects_before_launch():
+    f = L.la_prefill_fwd_varlen
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 10, 2, 2, 128, 128, 1.0, FAKE, None, 0, None, 0, 0, None) == \
+        la.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 3, 10, 2, 2, 128, 128, 1.0, FAKE, None, 0, None, 0, 0, None) == \
+        la.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 10, 2, 2, 128, 128, 1.0, FAKE, None, 0, None, 0, 7, None) == \
+        la.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 10, 2, 2, 96, 128, 1.0, FAKE, None, 0, None, 0, 0, None) == \
+        la.LA_ERR_UNSUPPORTED
+
+
+def test_commit_rejects_before_launch():
+    f = L.la_state_commit
+    assert f(FAKE, FAKE, 2, 8, 2, 2, 128, 128, FAKE, None, 4, FAKE, FAKE, None) == la.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 2, 8, 2, 2, 128, 128, FAKE, FAKE, 4, FAKE, None, None) == la.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 2, 8, 2, 3, 128, 128, FAKE, FAKE, 4, FAKE, FAKE, None) == la.LA_ERR_UNSUPPORTED
+
+
+def test_python_binding_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 64, 2, 128, dtype=torch.float16)
+    with pytest.raises((TypeError, ValueError)):
+        la.la_prefill_fwd(q, q, q, q, torch.zeros(2))
