@@ -85,6 +85,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (torch copy_) --steps times: the reference kernel that "
+                         "scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
@@ -97,8 +100,19 @@ def main():
     import la_synth
     import linear_attention_decay_amd as la
 
-    w = la_synth.config(args.config)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": args.steps}), flush=True)
+        return
+
+    w = la_synth.config(args.config)
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     q = to_dev(w.q).view(torch.bfloat16)
     k = to_dev(w.k).view(torch.bfloat16)

@@ -26,6 +26,10 @@ class LaError(RuntimeError):
 
 
 def _load():
+    # The library's HIP runtime dependency (soname libamdhip64.so.7) must resolve to the runtime the caller's
+    # torch already loaded; loading the library first would bring in a second HIP runtime whose device
+    # pointers and streams are not torch's. Import torch before dlopen so the soname is already satisfied.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"HIP library not built: {LIB_PATH} is missing; run __graft_entry__.build()")
     L = ctypes.CDLL(LIB_PATH)

@@ -44,11 +44,7 @@ constexpr int kD = 128;                   // key dim
 constexpr int kDV = 128;                  // value dim
 constexpr int kVSplit = 2;                // workgroups per (sequence, value head)
 constexpr int kVW = kDV / kVSplit;        // value columns per workgroup
-constexpr int kWaves = kVW / 16;          // one 16-column tile per wave
-constexpr int kThreads = kWaves * 64;
-
-constexpr int kQKStride = kD + 8;         // LDS row stride of staged Q/K rows (bf16 elements)
-constexpr int kVStride = kVW + 8;         // LDS row stride of staged V rows
+constexpr int kThreads = 512;             // 4 consumer waves (one 16-column value tile each) + 4 producer waves
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -112,13 +108,6 @@ __device__ __forceinline__ f32x4 mfma16(u32x2 a, s16x4 b, f32x4 c) {
 // lambda^n for n >= 0 given l2 = log2(lambda) (finite, <= 0).
 __device__ __forceinline__ float lam_pow(float l2, int n) { return __builtin_amdgcn_exp2f(l2 * (float)n); }
 
-__device__ __forceinline__ u32x4 ld_lds_frag_rows(const uint16_t *row, int col) {
-    // slots 0..3 = row[col .. col+3], slots 4..7 = row[col+16 .. col+19]
-    u32x2 a = *reinterpret_cast<const u32x2 *>(row + col);
-    u32x2 b = *reinterpret_cast<const u32x2 *>(row + col + 16);
-    return u32x4{a.x, a.y, b.x, b.y};
-}
-
 struct Unit {
     int32_t seq, hv, vpart;
 };
@@ -146,30 +135,119 @@ __device__ __forceinline__ Unit decode_unit(int u, const Params &p) {
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// the kernel
+// LDS layout. Q/K chunk tiles are 64 rows x 256 B, V tiles 64 rows x 128 B (one value half), stored with an
+// XOR swizzle of 16-byte segments so that the fragment reads (16 rows x 8 B per lane group) hit distinct
+// banks. P and K^T fragments are stored "fragment-native": 64 lanes x 16 B per block, read back by the same
+// lane layout.
+//   Q: 3 buffers (consumer reads chunk c-1, producer reads chunk c, chunk c+1 is being staged)
+//   K: 2 buffers (producer reads chunk c, chunk c+1 is being staged)
+//   V: 3 buffers (as Q)
+//   P, K^T: 2 buffers (producer writes chunk c, consumer reads chunk c-1)
+// ---------------------------------------------------------------------------------------------------------
+constexpr int kQKTileB = kC * kD * 2;        // 16384
+constexpr int kVTileB = kC * kVW * 2;        // 8192
+constexpr int kFragB = 64 * 16;              // one fragment block
+constexpr int kPBufB = 6 * 2 * kFragB;       // 6 lower-triangle (jt, i-pair) blocks, hi and lo
+constexpr int kKTBufB = 8 * 2 * kFragB;      // 8 key tiles x 2 token pairs
+constexpr int kOffQ = 0;
+constexpr int kOffK = kOffQ + 3 * kQKTileB;
+constexpr int kOffV = kOffK + 2 * kQKTileB;
+constexpr int kOffP = kOffV + 3 * kVTileB;
+constexpr int kOffKT = kOffP + 2 * kPBufB;
+constexpr int kLdsBytes = kOffKT + 2 * kKTBufB;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+
+__device__ __forceinline__ int qk_off(int r, int c) {      // byte offset of element (r, c) in a Q/K tile
+    return r * 256 + ((((c >> 3) ^ (r & 15))) << 4) + ((c & 7) << 1);
+}
+__device__ __forceinline__ int v_off(int r, int c) {       // byte offset of element (r, c) in a V tile
+    return r * 128 + ((((c >> 3) ^ ((r >> 1) & 7))) << 4) + ((c & 7) << 1);
+}
+// fragment of a Q/K tile: slots 0..3 = row r, columns c..c+3; slots 4..7 = columns c+16..c+19
+__device__ __forceinline__ u32x4 ld_frag_qk(const uint8_t *tile, int r, int c) {
+    const u32x2 a = *reinterpret_cast<const u32x2 *>(tile + qk_off(r, c));
+    const u32x2 b = *reinterpret_cast<const u32x2 *>(tile + qk_off(r, c + 16));
+    return u32x4{a.x, a.y, b.x, b.y};
+}
+__device__ __forceinline__ int p_blk(int jt, int ip) { return jt < 2 ? jt : 2 * jt - 2 + ip; }
+
+// ---------------------------------------------------------------------------------------------------------
+// Producer: scores A^T[i][j] = K_i . Q_j for the lower-triangle 16x16 tiles (it <= jt) a producer wave owns,
+// decay mask P = lambda^{j-i} A (i <= j), written as bf16 hi + lo fragments.
+//   wave 0: (0,3) (1,3) (2,3)   wave 1: (3,3) (0,2) (1,2)   wave 2: (2,2) (0,1)   wave 3: (1,1) (0,0)
+// Waves 2 and 3 also zero the strictly-upper halves of the (2,2) and (0,0) block pairs.
+// ---------------------------------------------------------------------------------------------------------
+// tile t of producer PW: it = bits [4t, 4t+2), jt = bits [4t+2, 4t+4) of code
+template <int PW> struct Tiles;
+template <> struct Tiles<0> { static constexpr int n = 3, code = 0 | (3 << 2) | (1 << 4) | (3 << 6) | (2 << 8) | (3 << 10); };
+template <> struct Tiles<1> { static constexpr int n = 3, code = 3 | (3 << 2) | (0 << 4) | (2 << 6) | (1 << 8) | (2 << 10); };
+template <> struct Tiles<2> { static constexpr int n = 2, code = 2 | (2 << 2) | (0 << 4) | (1 << 6); };
+template <> struct Tiles<3> { static constexpr int n = 2, code = 1 | (1 << 2) | (0 << 4) | (0 << 6); };
+template <int PW> __device__ __forceinline__ constexpr int tile_it(int t) { return (Tiles<PW>::code >> (4 * t)) & 3; }
+template <int PW> __device__ __forceinline__ constexpr int tile_jt(int t) { return (Tiles<PW>::code >> (4 * t + 2)) & 3; }
+
+template <int PW>
+__device__ __forceinline__ void score_factors(float (&pf)[12], float l2, int lr, int lg) {
+#pragma unroll
+    for (int t = 0; t < Tiles<PW>::n; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * tile_it<PW>(t) + 4 * lg + r, j = 16 * tile_jt<PW>(t) + lr;
+            pf[4 * t + r] = (i <= j) ? lam_pow(l2, j - i) : 0.f;
+        }
+}
+
+template <int PW>
+__device__ __forceinline__ void produce_scores(const float (&pf)[12], const uint8_t *tq, const uint8_t *tk,
+                                               uint8_t *pbuf, int lane, int lr, int lg) {
+#pragma unroll
+    for (int t = 0; t < Tiles<PW>::n; ++t) {
+        const int it = tile_it<PW>(t), jt = tile_jt<PW>(t);
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kp = 0; kp < 4; ++kp)
+            a = mfma32(ld_frag_qk(tk, 16 * it + lr, 32 * kp + 4 * lg), ld_frag_qk(tq, 16 * jt + lr, 32 * kp + 4 * lg), a);
+        const u32x2 a01 = split_bf16x2(a[0] * pf[4 * t + 0], a[1] * pf[4 * t + 1]);
+        const u32x2 a23 = split_bf16x2(a[2] * pf[4 * t + 2], a[3] * pf[4 * t + 3]);
+        uint8_t *dst = pbuf + (p_blk(jt, it >> 1) * 2) * kFragB + lane * 16 + 8 * (it & 1);
+        *reinterpret_cast<u32x2 *>(dst) = u32x2{a01.x, a23.x};
+        *reinterpret_cast<u32x2 *>(dst + kFragB) = u32x2{a01.y, a23.y};
+    }
+    if (PW == 2 || PW == 3) {
+        const int jt = PW == 3 ? 0 : 2;      // zero half (it = jt + 1) of the diagonal block pair
+        uint8_t *dst = pbuf + (p_blk(jt, jt >> 1) * 2) * kFragB + lane * 16 + 8;
+        *reinterpret_cast<u32x2 *>(dst) = u32x2{0, 0};
+        *reinterpret_cast<u32x2 *>(dst + kFragB) = u32x2{0, 0};
+    }
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// the kernel: 8 waves; waves 0..3 are consumers (state owners), waves 4..7 producers
 // ---------------------------------------------------------------------------------------------------------
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
     constexpr bool kOut = (MODE != kCommit);
-
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[kOut ? kC * kQKStride : 8];
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kC * kQKStride];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[kC * kVStride];
-    __shared__ __attribute__((aligned(16))) uint16_t sP[kOut ? 4 * 2 * 2 * 64 * 8 : 8];  // [jt][ipair][hi/lo][lane][8]
-    __shared__ __attribute__((aligned(16))) uint16_t sKT[8 * 2 * 64 * 8];                // [kt][ipair][lane][8]
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = tid >> 6;          // wave = 16-column value tile
-    const int lr = lane & 15;        // fragment row / accumulator column
-    const int lg = lane >> 4;        // slot group
-
-    // identity fragment for the 16x16x16 transposes: slot e of group g is 1 where 4g + e == lane % 16
-    s16x4 ident;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ident[e] = (4 * lg + e == lr) ? (short)0x3F80 : (short)0;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform: role branches are scalar
+    const bool consumer = w < 4;
+    const int cw = w & 3;            // consumer: value tile; producer: producer index
 
     for (int u = blockIdx.x; u < p.nunits; u += gridDim.x) {
+        // Lane indices are re-derived through an opaque copy in every unit iteration so that the compiler
+        // does not hoist lane-dependent set-up (decay exponents, masks) of both roles out of this loop and
+        // keep it live for the whole kernel.
+        int tid_u = tid;
+        asm volatile("" : "+v"(tid_u));
+        const int lane = tid_u & 63;
+        const int lr = lane & 15;
+        const int lg = lane >> 4;
+        const int ptid = tid_u - 256;      // producer thread index 0..255
+        s16x4 ident;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ident[e] = (4 * lg + e == lr) ? (short)0x3F80 : (short)0;
+
         const Unit un = decode_unit(u, p);
         const int h = un.hv / p.G;
         const int v0 = un.vpart * kVW;
@@ -199,234 +277,239 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
 
         float l2 = -p.slope[un.hv] * 1.4426950408889634f;
         l2 = fmaxf(l2, -1.0e30f);                                    // slope = +inf -> lambda^0 = 1, lambda^n = 0
-
-        // ---- initial state: S^T tiles, lane holds S[v][k..k+3], v = v0 + 16w + lr, k = 16kt + 4lg
-        f32x4 S[8];
-        float *plane = nullptr;
-        if (slot >= 0) plane = p.pool + ((int64_t)slot * p.HV + un.hv) * (kDV * kD);
-        const int vrow = v0 + 16 * w + lr;
-        if (slot >= 0 && (p.flags & LA_STATE_READ)) {
-#pragma unroll
-            for (int kt = 0; kt < 8; ++kt)
-                S[kt] = *reinterpret_cast<const f32x4 *>(plane + vrow * kD + 16 * kt + 4 * lg);
-        } else {
-#pragma unroll
-            for (int kt = 0; kt < 8; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-
         const int nch = (len + kC - 1) / kC;
+        const float dec64 = lam_pow(l2, kC);
         const int64_t qk_row_stride = (int64_t)p.H * kD;
         const int64_t v_row_stride = (int64_t)p.HV * kDV;
-        const uint16_t *qbase = p.q + (row0 * p.H + h) * kD;
-        const uint16_t *kbase = p.k + (row0 * p.H + h) * kD;
-        const uint16_t *vbase = p.v + (row0 * p.HV + un.hv) * kDV + v0;
 
-        // register prefetch of one chunk: Q/K 4 x 16 B each, V 2 x 16 B per thread
-        u32x4 pq[4], pk[4], pv[2];
-        auto prefetch = [&](int c) {
-            const int c0 = c * kC;
-            const int lc = min(kC, len - c0);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int seg = tid + kThreads * s;
-                const int r = seg >> 4, col = (seg & 15) * 8;
-                if (r < lc) {
-                    if (kOut) pq[s] = *reinterpret_cast<const u32x4 *>(qbase + (c0 + r) * qk_row_stride + col);
-                    pk[s] = *reinterpret_cast<const u32x4 *>(kbase + (c0 + r) * qk_row_stride + col);
-                } else {
-                    pq[s] = u32x4{0, 0, 0, 0};
-                    pk[s] = u32x4{0, 0, 0, 0};
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int seg = tid + kThreads * s;
-                const int r = seg >> 3, col = (seg & 7) * 8;
-                if (r < lc)
-                    pv[s] = *reinterpret_cast<const u32x4 *>(vbase + (c0 + r) * v_row_stride + col);
-                else
-                    pv[s] = u32x4{0, 0, 0, 0};
-            }
-        };
-        if (nch > 0) prefetch(0);
+        float *plane = nullptr;
+        if (slot >= 0) plane = p.pool + ((int64_t)slot * p.HV + un.hv) * (kDV * kD);
 
-        for (int c = 0; c < nch; ++c) {
-            const int c0 = c * kC;
-            const int lc = min(kC, len - c0);
-
-            // ---- stage chunk rows into LDS
+        // The two roles run separate loops with the same number of workgroup barriers (one before the chunk
+        // loop, one per iteration), so each role's loop-carried registers are allocated on their own.
+        if (consumer) {
+            // ======================================== consumer: owns S^T for value tile cw
+            // S^T tiles: lane holds S[v][k..k+3], v = v0 + 16cw + lr, k = 16kt + 4lg
+            f32x4 S[8];
+            float fvd[16];              // lambda^{63-i} for i = 16it+4lg+r (full chunk)
+            float finter[4];            // lambda^{j+1} for j = 16jt+lr
+            const int vrow = v0 + 16 * cw + lr;
+            if (slot >= 0 && (p.flags & LA_STATE_READ)) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int seg = tid + kThreads * s;
-                const int r = seg >> 4, col = (seg & 15) * 8;
-                if (kOut) *reinterpret_cast<u32x4 *>(sQ + r * kQKStride + col) = pq[s];
-                *reinterpret_cast<u32x4 *>(sK + r * kQKStride + col) = pk[s];
+                for (int kt = 0; kt < 8; ++kt)
+                    S[kt] = *reinterpret_cast<const f32x4 *>(plane + vrow * kD + 16 * kt + 4 * lg);
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int seg = tid + kThreads * s;
-                const int r = seg >> 3, col = (seg & 7) * 8;
-                *reinterpret_cast<u32x4 *>(sV + r * kVStride + col) = pv[s];
-            }
+            for (int it = 0; it < 4; ++it)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) fvd[4 * it + r] = lam_pow(l2, 63 - (16 * it + 4 * lg + r));
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) finter[jt] = lam_pow(l2, 16 * jt + lr + 1);
             __syncthreads();
-            if (c + 1 < nch) prefetch(c + 1);
 
-            // ============ phase A: everything that does not need this chunk's state update ============
-            f32x4 acc[4];            // O^T tiles [v 16][j 16] for jt = 0..3
-            u32x4 qf[4][4];          // Q fragments [jt][kpair]
-            if (kOut) {
-#pragma unroll
-                for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-                    for (int kp = 0; kp < 4; ++kp)
-                        qf[jt][kp] = ld_lds_frag_rows(sQ + (16 * jt + lr) * kQKStride, 32 * kp + 4 * lg);
+            for (int t = 0; t <= nch; ++t) {
+                if (t > 0) {
+                    const int c = t - 1;
+                    const int c0 = c * kC;
+                    const int lc = min(kC, len - c0);
+                    const uint8_t *tq = smem + kOffQ + (c % 3) * kQKTileB;
+                    const uint8_t *tv = smem + kOffV + (c % 3) * kVTileB;
+                    const uint8_t *pbuf = smem + kOffP + (c & 1) * kPBufB;
+                    const uint8_t *ktbuf = smem + kOffKT + (c & 1) * kKTBufB;
 
-                // history term Q S^T with S = hi + lo
-                u32x4 shi[4], slo[4];
+                    // V^T fragments of this wave's value tile, and V_dec = lambda^{lc-1-i} v_i as hi + lo
+                    u32x4 vf[2], vdh[2], vdl[2];
 #pragma unroll
-                for (int kp = 0; kp < 4; ++kp) {
-                    const u32x2 a = split_bf16x2(S[2 * kp][0], S[2 * kp][1]);
-                    const u32x2 b = split_bf16x2(S[2 * kp][2], S[2 * kp][3]);
-                    const u32x2 c = split_bf16x2(S[2 * kp + 1][0], S[2 * kp + 1][1]);
-                    const u32x2 d = split_bf16x2(S[2 * kp + 1][2], S[2 * kp + 1][3]);
-                    shi[kp] = u32x4{a.x, b.x, c.x, d.x};
-                    slo[kp] = u32x4{a.y, b.y, c.y, d.y};
-                }
+                    for (int it = 0; it < 4; ++it) {
+                        const u32x2 a = *reinterpret_cast<const u32x2 *>(tv + v_off(16 * it + lr, 16 * cw + 4 * lg));
+                        const f32x4 x = mfma16(a, ident, f32x4{0.f, 0.f, 0.f, 0.f});
+                        float d[4];
 #pragma unroll
-                for (int jt = 0; jt < 4; ++jt) {
-                    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kp = 0; kp < 4; ++kp) {
-                        a = mfma32(shi[kp], qf[jt][kp], a);
-                        a = mfma32(slo[kp], qf[jt][kp], a);
-                    }
-                    acc[jt] = a;
-                }
-
-                // scores A^T[i][j] for i-tile it = w, j-tiles jt >= w; decay mask; P = hi + lo into LDS
-                {
-                    const int it = w;
-                    u32x4 kf[4];
-#pragma unroll
-                    for (int kp = 0; kp < 4; ++kp)
-                        kf[kp] = ld_lds_frag_rows(sK + (16 * it + lr) * kQKStride, 32 * kp + 4 * lg);
-#pragma unroll
-                    for (int jt = 0; jt < 4; ++jt) {
-                        uint16_t *dst_hi = sP + (((jt * 2 + (it >> 1)) * 2 + 0) * 64 + lane) * 8 + 4 * (it & 1);
-                        uint16_t *dst_lo = sP + (((jt * 2 + (it >> 1)) * 2 + 1) * 64 + lane) * 8 + 4 * (it & 1);
-                        if (jt >= it) {
-                            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                            for (int kp = 0; kp < 4; ++kp) a = mfma32(kf[kp], qf[jt][kp], a);
-                            const int j = 16 * jt + lr;
-                            float pv4[4];
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
+                        for (int r = 0; r < 4; ++r) {
+                            float f = fvd[4 * it + r];
+                            if (lc != kC) {
                                 const int i = 16 * it + 4 * lg + r;
-                                pv4[r] = (i <= j) ? a[r] * lam_pow(l2, j - i) : 0.f;
+                                f = (i < lc) ? lam_pow(l2, lc - 1 - i) : 0.f;
                             }
-                            const u32x2 a01 = split_bf16x2(pv4[0], pv4[1]);
-                            const u32x2 a23 = split_bf16x2(pv4[2], pv4[3]);
-                            *reinterpret_cast<u32x2 *>(dst_hi) = u32x2{a01.x, a23.x};
-                            *reinterpret_cast<u32x2 *>(dst_lo) = u32x2{a01.y, a23.y};
-                        } else if (jt == it - 1 && (it & 1)) {
-                            // upper half of a diagonal block pair: zero
-                            *reinterpret_cast<u32x2 *>(dst_hi) = u32x2{0, 0};
-                            *reinterpret_cast<u32x2 *>(dst_lo) = u32x2{0, 0};
+                            d[r] = x[r] * f;
+                        }
+                        const uint32_t x0 = pack_bf16x2(x[0], x[1]), x1 = pack_bf16x2(x[2], x[3]);
+                        const u32x2 d01 = split_bf16x2(d[0], d[1]);
+                        const u32x2 d23 = split_bf16x2(d[2], d[3]);
+                        if ((it & 1) == 0) {
+                            vf[it >> 1].x = x0; vf[it >> 1].y = x1;
+                            vdh[it >> 1].x = d01.x; vdh[it >> 1].y = d23.x;
+                            vdl[it >> 1].x = d01.y; vdl[it >> 1].y = d23.y;
+                        } else {
+                            vf[it >> 1].z = x0; vf[it >> 1].w = x1;
+                            vdh[it >> 1].z = d01.x; vdh[it >> 1].w = d23.x;
+                            vdl[it >> 1].z = d01.y; vdl[it >> 1].w = d23.y;
+                        }
+                    }
+
+                    if (kOut) {
+                        // history term Q S^T with S = hi + lo (state before this chunk)
+                        u32x4 shi[4], slo[4];
+#pragma unroll
+                        for (int kp = 0; kp < 4; ++kp) {
+                            const u32x2 a = split_bf16x2(S[2 * kp][0], S[2 * kp][1]);
+                            const u32x2 b2 = split_bf16x2(S[2 * kp][2], S[2 * kp][3]);
+                            const u32x2 c2 = split_bf16x2(S[2 * kp + 1][0], S[2 * kp + 1][1]);
+                            const u32x2 d2 = split_bf16x2(S[2 * kp + 1][2], S[2 * kp + 1][3]);
+                            shi[kp] = u32x4{a.x, b2.x, c2.x, d2.x};
+                            slo[kp] = u32x4{a.y, b2.y, c2.y, d2.y};
+                        }
+                        f32x4 acc[4];
+#pragma unroll
+                        for (int jt = 0; jt < 4; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kp = 0; kp < 4; ++kp)
+#pragma unroll
+                            for (int jt = 0; jt < 4; ++jt) {
+                                const u32x4 qf = ld_frag_qk(tq, 16 * jt + lr, 32 * kp + 4 * lg);
+                                acc[jt] = mfma32(shi[kp], qf, acc[jt]);
+                                acc[jt] = mfma32(slo[kp], qf, acc[jt]);
+                            }
+                        // within-chunk term P.V, then O = scale (lambda^{j+1} history + within)
+                        const float sc = p.scale;
+                        uint16_t *obase = p.o + ((row0 + c0) * p.HV + un.hv) * kDV + v0 + 16 * cw + 4 * lg;
+#pragma unroll
+                        for (int jt = 0; jt < 4; ++jt) {
+                            f32x4 a = acc[jt] * finter[jt];
+#pragma unroll
+                            for (int ip = 0; ip <= (jt >> 1); ++ip) {
+                                const uint8_t *blk = pbuf + p_blk(jt, ip) * 2 * kFragB + lane * 16;
+                                a = mfma32(vf[ip], *reinterpret_cast<const u32x4 *>(blk), a);
+                                a = mfma32(vf[ip], *reinterpret_cast<const u32x4 *>(blk + kFragB), a);
+                            }
+                            const int j = 16 * jt + lr;
+                            if (j < lc) {
+                                const u32x2 ov = {pack_bf16x2(sc * a[0], sc * a[1]), pack_bf16x2(sc * a[2], sc * a[3])};
+                                *reinterpret_cast<u32x2 *>(obase + (int64_t)j * v_row_stride) = ov;
+                            }
+                        }
+                    }
+
+                    // state update S <- lambda^{lc} S + K^T V_dec
+                    const float dec = (lc == kC) ? dec64 : lam_pow(l2, lc);
+#pragma unroll
+                    for (int kt = 0; kt < 8; ++kt) S[kt] = S[kt] * dec;
+#pragma unroll
+                    for (int ip = 0; ip < 2; ++ip)
+#pragma unroll
+                        for (int kt = 0; kt < 8; ++kt) {
+                            const u32x4 kf = *reinterpret_cast<const u32x4 *>(ktbuf + ((kt * 2 + ip) * 64 + lane) * 16);
+                            S[kt] = mfma32(kf, vdh[ip], S[kt]);
+                            S[kt] = mfma32(kf, vdl[ip], S[kt]);
+                        }
+                }
+                __syncthreads();
+            }
+
+            if (slot >= 0 && (p.flags & LA_STATE_WRITE)) {
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt)
+                    *reinterpret_cast<f32x4 *>(plane + vrow * kD + 16 * kt + 4 * lg) = S[kt];
+            }
+        } else {
+            // ======================================== producer: staging, scores / P, K^T
+            float pf[12];               // score decay factors of this wave's tiles
+            u32x4 pq[4], pk[4], pv[2];  // one chunk of rows in flight
+            const uint16_t *qbase = p.q + (row0 * p.H + h) * kD;
+            const uint16_t *kbase = p.k + (row0 * p.H + h) * kD;
+            const uint16_t *vbase = p.v + (row0 * p.HV + un.hv) * kDV + v0;
+            auto prefetch = [&](int c) {
+                const int c0 = c * kC;
+                const int lc = min(kC, len - c0);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int seg = ptid + 256 * s;
+                    const int r = seg >> 4, col = (seg & 15) * 8;
+                    if (r < lc) {
+                        if (kOut) pq[s] = *reinterpret_cast<const u32x4 *>(qbase + (c0 + r) * qk_row_stride + col);
+                        pk[s] = *reinterpret_cast<const u32x4 *>(kbase + (c0 + r) * qk_row_stride + col);
+                    } else {
+                        pq[s] = u32x4{0, 0, 0, 0};
+                        pk[s] = u32x4{0, 0, 0, 0};
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int seg = ptid + 256 * s;
+                    const int r = seg >> 3, col = (seg & 7) * 8;
+                    pv[s] = (r < lc) ? *reinterpret_cast<const u32x4 *>(vbase + (c0 + r) * v_row_stride + col)
+                                     : u32x4{0, 0, 0, 0};
+                }
+            };
+            auto stage = [&](int c) {
+                uint8_t *tq = smem + kOffQ + (c % 3) * kQKTileB;
+                uint8_t *tk = smem + kOffK + (c & 1) * kQKTileB;
+                uint8_t *tv = smem + kOffV + (c % 3) * kVTileB;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int seg = ptid + 256 * s;
+                    const int r = seg >> 4, col = (seg & 15) * 8;
+                    if (kOut) *reinterpret_cast<u32x4 *>(tq + qk_off(r, col)) = pq[s];
+                    *reinterpret_cast<u32x4 *>(tk + qk_off(r, col)) = pk[s];
+                }
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int seg = ptid + 256 * s;
+                    const int r = seg >> 3, col = (seg & 7) * 8;
+                    *reinterpret_cast<u32x4 *>(tv + v_off(r, col)) = pv[s];
+                }
+            };
+
+            if (kOut) {
+                switch (cw) {
+                case 0: score_factors<0>(pf, l2, lr, lg); break;
+                case 1: score_factors<1>(pf, l2, lr, lg); break;
+                case 2: score_factors<2>(pf, l2, lr, lg); break;
+                default: score_factors<3>(pf, l2, lr, lg); break;
+                }
+            }
+            if (nch > 0) {
+                prefetch(0);
+                stage(0);
+            }
+            if (nch > 1) prefetch(1);
+            __syncthreads();
+
+            for (int t = 0; t <= nch; ++t) {
+                if (t + 1 < nch) stage(t + 1);
+                if (t + 2 < nch) prefetch(t + 2);
+                if (t < nch) {
+                    const uint8_t *tq = smem + kOffQ + (t % 3) * kQKTileB;
+                    const uint8_t *tk = smem + kOffK + (t & 1) * kQKTileB;
+                    if (kOut) {
+                        uint8_t *pbuf = smem + kOffP + (t & 1) * kPBufB;
+                        switch (cw) {
+                        case 0: produce_scores<0>(pf, tq, tk, pbuf, lane, lr, lg); break;
+                        case 1: produce_scores<1>(pf, tq, tk, pbuf, lane, lr, lg); break;
+                        case 2: produce_scores<2>(pf, tq, tk, pbuf, lane, lr, lg); break;
+                        default: produce_scores<3>(pf, tq, tk, pbuf, lane, lr, lg); break;
+                        }
+                    }
+                    // K^T fragments (exact bf16) for key tiles 2cw, 2cw+1
+                    uint8_t *ktbuf = smem + kOffKT + (t & 1) * kKTBufB;
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const int kt = 2 * cw + kk;
+#pragma unroll
+                        for (int it = 0; it < 4; ++it) {
+                            const u32x2 a = *reinterpret_cast<const u32x2 *>(tk + qk_off(16 * it + lr, 16 * kt + 4 * lg));
+                            const f32x4 x = mfma16(a, ident, f32x4{0.f, 0.f, 0.f, 0.f});
+                            *reinterpret_cast<u32x2 *>(ktbuf + ((kt * 2 + (it >> 1)) * 64 + lane) * 16 + 8 * (it & 1)) =
+                                u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
                         }
                     }
                 }
+                __syncthreads();
             }
-
-            // K^T fragments (exact bf16) for key tiles kt = 2w, 2w+1, all token tiles, into LDS
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int kt = 2 * w + kk;
-#pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const u32x2 a = *reinterpret_cast<const u32x2 *>(sK + (16 * it + lr) * kQKStride + 16 * kt + 4 * lg);
-                    const f32x4 t = mfma16(a, ident, f32x4{0.f, 0.f, 0.f, 0.f});
-                    u32x2 pk2 = {pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
-                    *reinterpret_cast<u32x2 *>(sKT + ((kt * 2 + (it >> 1)) * 64 + lane) * 8 + 4 * (it & 1)) = pk2;
-                }
-            }
-
-            // V^T fragments for this wave's value tile; decayed copy V_dec = lambda^{lc-1-i} v_i as hi + lo
-            u32x4 vf[2], vdh[2], vdl[2];
-#pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const u32x2 a = *reinterpret_cast<const u32x2 *>(sV + (16 * it + lr) * kVStride + 16 * w + 4 * lg);
-                const f32x4 t = mfma16(a, ident, f32x4{0.f, 0.f, 0.f, 0.f});
-                float d[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * it + 4 * lg + r;
-                    d[r] = (i < lc) ? t[r] * lam_pow(l2, lc - 1 - i) : 0.f;
-                }
-                const uint32_t x0 = pack_bf16x2(t[0], t[1]), x1 = pack_bf16x2(t[2], t[3]);
-                const u32x2 d01 = split_bf16x2(d[0], d[1]);
-                const u32x2 d23 = split_bf16x2(d[2], d[3]);
-                const uint32_t h0 = d01.x, l0 = d01.y, h1 = d23.x, l1 = d23.y;
-                if ((it & 1) == 0) {
-                    vf[it >> 1].x = x0; vf[it >> 1].y = x1;
-                    vdh[it >> 1].x = h0; vdh[it >> 1].y = h1;
-                    vdl[it >> 1].x = l0; vdl[it >> 1].y = l1;
-                } else {
-                    vf[it >> 1].z = x0; vf[it >> 1].w = x1;
-                    vdh[it >> 1].z = h0; vdh[it >> 1].w = h1;
-                    vdl[it >> 1].z = l0; vdl[it >> 1].w = l1;
-                }
-            }
-            __syncthreads();
-
-            // ============ phase B: within-chunk term, output, state update ============
-            if (kOut) {
-                const float sc = p.scale;
-                uint16_t *obase = p.o + ((row0 + c0) * p.HV + un.hv) * kDV + v0 + 16 * w + 4 * lg;
-#pragma unroll
-                for (int jt = 0; jt < 4; ++jt) {
-                    const int j = 16 * jt + lr;
-                    const float fj = lam_pow(l2, j + 1);
-                    f32x4 a = acc[jt] * fj;
-#pragma unroll
-                    for (int ip = 0; ip <= (jt >> 1); ++ip) {
-                        const u32x4 ph = *reinterpret_cast<const u32x4 *>(sP + (((jt * 2 + ip) * 2 + 0) * 64 + lane) * 8);
-                        const u32x4 pl = *reinterpret_cast<const u32x4 *>(sP + (((jt * 2 + ip) * 2 + 1) * 64 + lane) * 8);
-                        a = mfma32(vf[ip], ph, a);
-                        a = mfma32(vf[ip], pl, a);
-                    }
-                    if (j < lc) {
-                        u32x2 ov = {pack_bf16x2(sc * a[0], sc * a[1]), pack_bf16x2(sc * a[2], sc * a[3])};
-                        *reinterpret_cast<u32x2 *>(obase + (int64_t)j * v_row_stride) = ov;
-                    }
-                }
-            }
-
-            {
-                const float dec = lam_pow(l2, lc);
-#pragma unroll
-                for (int kt = 0; kt < 8; ++kt) {
-                    f32x4 s = S[kt] * dec;
-#pragma unroll
-                    for (int ip = 0; ip < 2; ++ip) {
-                        const u32x4 kf = *reinterpret_cast<const u32x4 *>(sKT + ((kt * 2 + ip) * 64 + lane) * 8);
-                        s = mfma32(kf, vdh[ip], s);
-                        s = mfma32(kf, vdl[ip], s);
-                    }
-                    S[kt] = s;
-                }
-            }
-            // No barrier here: the next writes to sP / sKT come after the next staging barrier, which every
-            // wave reaches only after finishing this phase.
         }
-
-        // ---- final state
-        if (slot >= 0 && (p.flags & LA_STATE_WRITE)) {
-#pragma unroll
-            for (int kt = 0; kt < 8; ++kt)
-                *reinterpret_cast<f32x4 *>(plane + vrow * kD + 16 * kt + 4 * lg) = S[kt];
-        }
-        __syncthreads();   // LDS is reused by the next unit of a persistent workgroup
     }
 }
 
