@@ -135,90 +135,103 @@ __device__ __forceinline__ Unit decode_unit(int u, const Params &p) {
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// LDS layout. Q/K chunk tiles are 64 rows x 256 B, V tiles 64 rows x 128 B (one value half), stored with an
-// XOR swizzle of 16-byte segments so that the fragment reads (16 rows x 8 B per lane group) hit distinct
-// banks. P and K^T fragments are stored "fragment-native": 64 lanes x 16 B per block, read back by the same
-// lane layout.
-//   Q: 3 buffers (consumer reads chunk c-1, producer reads chunk c, chunk c+1 is being staged)
-//   K: 2 buffers (producer reads chunk c, chunk c+1 is being staged)
-//   V: 3 buffers (as Q)
-//   P, K^T: 2 buffers (producer writes chunk c, consumer reads chunk c-1)
+// LDS layout (one workgroup per CU; 144 KiB).
+//   Q, K tiles: 64 rows x 256 B; V tiles (one value half): 64 rows x 128 B. Row-major as in HBM, with the
+//   16-byte segments of row r stored at segment index (seg XOR (r % 16)) for Q/K and (seg XOR ((r/2) % 8))
+//   for V, so that 16-row fragment reads and transposing reads spread over all banks. The tiles are filled
+//   by buffer loads that write LDS directly; the XOR is applied on the source side (lane -> segment), and
+//   rows past the end of a sequence fall outside the buffer range and arrive as zeros.
+//   Q, K, V: 3 buffers each (the consumers read chunk c-1, the producers chunk c, chunk c+1 is in flight).
+//   P: 2 buffers of 6 lower-triangle (jt, token-pair) fragment blocks, hi and lo, 64 lanes x 16 B each.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kQKTileB = kC * kD * 2;        // 16384
 constexpr int kVTileB = kC * kVW * 2;        // 8192
 constexpr int kFragB = 64 * 16;              // one fragment block
-constexpr int kPBufB = 6 * 2 * kFragB;       // 6 lower-triangle (jt, i-pair) blocks, hi and lo
-constexpr int kKTBufB = 8 * 2 * kFragB;      // 8 key tiles x 2 token pairs
+constexpr int kPBufB = 6 * 2 * kFragB;       // 12288
 constexpr int kOffQ = 0;
 constexpr int kOffK = kOffQ + 3 * kQKTileB;
-constexpr int kOffV = kOffK + 2 * kQKTileB;
+constexpr int kOffV = kOffK + 3 * kQKTileB;
 constexpr int kOffP = kOffV + 3 * kVTileB;
-constexpr int kOffKT = kOffP + 2 * kPBufB;
-constexpr int kLdsBytes = kOffKT + 2 * kKTBufB;
+constexpr int kLdsBytes = kOffP + 2 * kPBufB;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
-__device__ __forceinline__ int qk_off(int r, int c) {      // byte offset of element (r, c) in a Q/K tile
-    return r * 256 + ((((c >> 3) ^ (r & 15))) << 4) + ((c & 7) << 1);
+constexpr int kBufDword3 = 0x00020000;       // buffer resource word 3: raw 32-bit data format
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ int qk_seg_off(int r, int seg) { return r * 256 + ((seg ^ (r & 15)) << 4); }
+__device__ __forceinline__ int v_seg_off(int r, int seg) { return r * 128 + ((seg ^ ((r >> 1) & 7)) << 4); }
+
+// 8 consecutive elements of a Q/K row: columns 8*seg .. 8*seg+7
+__device__ __forceinline__ u32x4 ld_row8(const uint8_t *tile, int r, int seg) {
+    return *reinterpret_cast<const u32x4 *>(tile + qk_seg_off(r, seg));
 }
-__device__ __forceinline__ int v_off(int r, int c) {       // byte offset of element (r, c) in a V tile
-    return r * 128 + ((((c >> 3) ^ ((r >> 1) & 7))) << 4) + ((c & 7) << 1);
-}
-// fragment of a Q/K tile: slots 0..3 = row r, columns c..c+3; slots 4..7 = columns c+16..c+19
-__device__ __forceinline__ u32x4 ld_frag_qk(const uint8_t *tile, int r, int c) {
-    const u32x2 a = *reinterpret_cast<const u32x2 *>(tile + qk_off(r, c));
-    const u32x2 b = *reinterpret_cast<const u32x2 *>(tile + qk_off(r, c + 16));
-    return u32x4{a.x, a.y, b.x, b.y};
+// transposing read: see ld_kt_frag
+__device__ __forceinline__ u32x2 ld_tr(const uint8_t *p) {
+    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, x);
 }
 __device__ __forceinline__ int p_blk(int jt, int ip) { return jt < 2 ? jt : 2 * jt - 2 + ip; }
 
 // ---------------------------------------------------------------------------------------------------------
-// Producer: scores A^T[i][j] = K_i . Q_j for the lower-triangle 16x16 tiles (it <= jt) a producer wave owns,
-// decay mask P = lambda^{j-i} A (i <= j), written as bf16 hi + lo fragments.
-//   wave 0: (0,3) (1,3) (2,3)   wave 1: (3,3) (0,2) (1,2)   wave 2: (2,2) (0,1)   wave 3: (1,1) (0,0)
-// Waves 2 and 3 also zero the strictly-upper halves of the (2,2) and (0,0) block pairs.
+// Producer: scores A^T[i][j] = K_i . Q_j for the lower-triangle 16x16 tiles of the block it in
+// [IT0, IT0+NI), jt in [JT0, JT0+NJ), with the d-contraction taken over 8 consecutive columns per slot
+// group; decay mask P = scale lambda^{j-i} A (i <= j) stored as bf16 hi + lo fragments; a strictly-upper
+// tile inside a diagonal block pair is stored as zeros.
+//   producer 0: (0..1, 2)   producer 1: (0..1, 3)   producer 2: (2..3, 2..3)   producer 3: (0..1, 0..1)
 // ---------------------------------------------------------------------------------------------------------
-// tile t of producer PW: it = bits [4t, 4t+2), jt = bits [4t+2, 4t+4) of code
-template <int PW> struct Tiles;
-template <> struct Tiles<0> { static constexpr int n = 3, code = 0 | (3 << 2) | (1 << 4) | (3 << 6) | (2 << 8) | (3 << 10); };
-template <> struct Tiles<1> { static constexpr int n = 3, code = 3 | (3 << 2) | (0 << 4) | (2 << 6) | (1 << 8) | (2 << 10); };
-template <> struct Tiles<2> { static constexpr int n = 2, code = 2 | (2 << 2) | (0 << 4) | (1 << 6); };
-template <> struct Tiles<3> { static constexpr int n = 2, code = 1 | (1 << 2) | (0 << 4) | (0 << 6); };
-template <int PW> __device__ __forceinline__ constexpr int tile_it(int t) { return (Tiles<PW>::code >> (4 * t)) & 3; }
-template <int PW> __device__ __forceinline__ constexpr int tile_jt(int t) { return (Tiles<PW>::code >> (4 * t + 2)) & 3; }
-
-template <int PW>
-__device__ __forceinline__ void score_factors(float (&pf)[12], float l2, int lr, int lg) {
+template <int IT0, int NI, int JT0, int NJ>
+__device__ __forceinline__ void score_factors(float (&pf)[16], float l2, float scale, int lr, int lg) {
 #pragma unroll
-    for (int t = 0; t < Tiles<PW>::n; ++t)
+    for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * tile_it<PW>(t) + 4 * lg + r, j = 16 * tile_jt<PW>(t) + lr;
-            pf[4 * t + r] = (i <= j) ? lam_pow(l2, j - i) : 0.f;
-        }
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * (IT0 + ii) + 4 * lg + r, j = 16 * (JT0 + jj) + lr;
+                pf[4 * (NJ * ii + jj) + r] = (IT0 + ii <= JT0 + jj && i <= j) ? scale * lam_pow(l2, j - i) : 0.f;
+            }
 }
 
-template <int PW>
-__device__ __forceinline__ void produce_scores(const float (&pf)[12], const uint8_t *tq, const uint8_t *tk,
+template <int IT0, int NI, int JT0, int NJ>
+__device__ __forceinline__ void produce_scores(const float (&pf)[16], const uint8_t *tq, const uint8_t *tk,
                                                uint8_t *pbuf, int lane, int lr, int lg) {
+    f32x4 a[NI][NJ];
 #pragma unroll
-    for (int t = 0; t < Tiles<PW>::n; ++t) {
-        const int it = tile_it<PW>(t), jt = tile_jt<PW>(t);
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
-        for (int kp = 0; kp < 4; ++kp)
-            a = mfma32(ld_frag_qk(tk, 16 * it + lr, 32 * kp + 4 * lg), ld_frag_qk(tq, 16 * jt + lr, 32 * kp + 4 * lg), a);
-        const u32x2 a01 = split_bf16x2(a[0] * pf[4 * t + 0], a[1] * pf[4 * t + 1]);
-        const u32x2 a23 = split_bf16x2(a[2] * pf[4 * t + 2], a[3] * pf[4 * t + 3]);
-        uint8_t *dst = pbuf + (p_blk(jt, it >> 1) * 2) * kFragB + lane * 16 + 8 * (it & 1);
-        *reinterpret_cast<u32x2 *>(dst) = u32x2{a01.x, a23.x};
-        *reinterpret_cast<u32x2 *>(dst + kFragB) = u32x2{a01.y, a23.y};
+        for (int jj = 0; jj < NJ; ++jj) a[ii][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+        u32x4 kf[NI], qf[NJ];
+#pragma unroll
+        for (int x = 0; x < NI; ++x) kf[x] = ld_row8(tk, 16 * (IT0 + x) + lr, 4 * kp + lg);
+#pragma unroll
+        for (int x = 0; x < NJ; ++x) qf[x] = ld_row8(tq, 16 * (JT0 + x) + lr, 4 * kp + lg);
+#pragma unroll
+        for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj)
+                if (IT0 + ii <= JT0 + jj) a[ii][jj] = mfma32(kf[ii], qf[jj], a[ii][jj]);
     }
-    if (PW == 2 || PW == 3) {
-        const int jt = PW == 3 ? 0 : 2;      // zero half (it = jt + 1) of the diagonal block pair
-        uint8_t *dst = pbuf + (p_blk(jt, jt >> 1) * 2) * kFragB + lane * 16 + 8;
-        *reinterpret_cast<u32x2 *>(dst) = u32x2{0, 0};
-        *reinterpret_cast<u32x2 *>(dst + kFragB) = u32x2{0, 0};
-    }
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+            const int it = IT0 + ii, jt = JT0 + jj;
+            uint8_t *dst = pbuf + (p_blk(jt, it >> 1) * 2) * kFragB + lane * 16 + 8 * (it & 1);
+            if (it <= jt) {
+                const float *f = &pf[4 * (NJ * ii + jj)];
+                const u32x2 a01 = split_bf16x2(a[ii][jj][0] * f[0], a[ii][jj][1] * f[1]);
+                const u32x2 a23 = split_bf16x2(a[ii][jj][2] * f[2], a[ii][jj][3] * f[3]);
+                *reinterpret_cast<u32x2 *>(dst) = u32x2{a01.x, a23.x};
+                *reinterpret_cast<u32x2 *>(dst + kFragB) = u32x2{a01.y, a23.y};
+            } else if (it == jt + 1 && (jt & 1) == 0) {
+                *reinterpret_cast<u32x2 *>(dst) = u32x2{0, 0};
+                *reinterpret_cast<u32x2 *>(dst + kFragB) = u32x2{0, 0};
+            }
+        }
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -227,7 +240,7 @@ __device__ __forceinline__ void produce_scores(const float (&pf)[12], const uint
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
     constexpr bool kOut = (MODE != kCommit);
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform: role branches are scalar
@@ -243,10 +256,6 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
         const int lane = tid_u & 63;
         const int lr = lane & 15;
         const int lg = lane >> 4;
-        const int ptid = tid_u - 256;      // producer thread index 0..255
-        s16x4 ident;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ident[e] = (4 * lg + e == lr) ? (short)0x3F80 : (short)0;
 
         const Unit un = decode_unit(u, p);
         const int h = un.hv / p.G;
@@ -279,25 +288,27 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
         l2 = fmaxf(l2, -1.0e30f);                                    // slope = +inf -> lambda^0 = 1, lambda^n = 0
         const int nch = (len + kC - 1) / kC;
         const float dec64 = lam_pow(l2, kC);
-        const int64_t qk_row_stride = (int64_t)p.H * kD;
-        const int64_t v_row_stride = (int64_t)p.HV * kDV;
-
+        const int qk_stride = p.H * kD * 2;                          // bytes between token rows
+        const int v_stride = p.HV * kDV * 2;
         float *plane = nullptr;
         if (slot >= 0) plane = p.pool + ((int64_t)slot * p.HV + un.hv) * (kDV * kD);
 
         // The two roles run separate loops with the same number of workgroup barriers (one before the chunk
         // loop, one per iteration), so each role's loop-carried registers are allocated on their own.
         if (consumer) {
-            // ======================================== consumer: owns S^T for value tile cw
-            // S^T tiles: lane holds S[v][k..k+3], v = v0 + 16cw + lr, k = 16kt + 4lg
+            // ======================================== consumer: owns the state rows of value tile cw
+            // State tiles S[kt] (kt = 0..7), lane holds S[v][k] for v = v0 + 16cw + lr and the four keys
+            // k = kappa(kt, 4lg + r) = 32(kt/2) + 8lg + 4(kt%2) + r, r = 0..3: the key order inside a tile is
+            // chosen (through the transposing K reads below) so that tiles 2s and 2s+1 together give each lane
+            // 8 consecutive keys -- the slot layout of a plain 16-byte Q row read.
             f32x4 S[8];
             float fvd[16];              // lambda^{63-i} for i = 16it+4lg+r (full chunk)
-            float finter[4];            // lambda^{j+1} for j = 16jt+lr
+            float finter[4];            // scale lambda^{j+1} for j = 16jt+lr
             const int vrow = v0 + 16 * cw + lr;
             if (slot >= 0 && (p.flags & LA_STATE_READ)) {
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt)
-                    S[kt] = *reinterpret_cast<const f32x4 *>(plane + vrow * kD + 16 * kt + 4 * lg);
+                    S[kt] = *reinterpret_cast<const f32x4 *>(plane + vrow * kD + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1));
             } else {
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -307,7 +318,17 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) fvd[4 * it + r] = lam_pow(l2, 63 - (16 * it + 4 * lg + r));
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) finter[jt] = lam_pow(l2, 16 * jt + lr + 1);
+            for (int jt = 0; jt < 4; ++jt) finter[jt] = p.scale * lam_pow(l2, 16 * jt + lr + 1);
+            s16x4 ident;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ident[e] = (4 * lg + e == lr) ? (short)0x3F80 : (short)0;
+            // transposing K reads: source lane (lg, lr) supplies row 4lg + lr/4 (+ token-pair and half
+            // offsets) and the 4 keys 32s + 8(lr%4) + 4(kt%2) .. +3; the instruction hands lane lr of each
+            // 16-lane group key kappa(kt, lr) of the 4 rows of its group.
+            const int tr_row = 4 * lg + (lr >> 2);
+            int tr_off[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) tr_off[s] = qk_seg_off(tr_row, 4 * s + (lr & 3));
             __syncthreads();
 
             for (int t = 0; t <= nch; ++t) {
@@ -316,25 +337,26 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                     const int c0 = c * kC;
                     const int lc = min(kC, len - c0);
                     const uint8_t *tq = smem + kOffQ + (c % 3) * kQKTileB;
+                    const uint8_t *tk = smem + kOffK + (c % 3) * kQKTileB;
                     const uint8_t *tv = smem + kOffV + (c % 3) * kVTileB;
                     const uint8_t *pbuf = smem + kOffP + (c & 1) * kPBufB;
-                    const uint8_t *ktbuf = smem + kOffKT + (c & 1) * kKTBufB;
 
                     // V^T fragments of this wave's value tile, and V_dec = lambda^{lc-1-i} v_i as hi + lo
                     u32x4 vf[2], vdh[2], vdl[2];
 #pragma unroll
                     for (int it = 0; it < 4; ++it) {
-                        const u32x2 a = *reinterpret_cast<const u32x2 *>(tv + v_off(16 * it + lr, 16 * cw + 4 * lg));
+                        const int r = 16 * it + lr;
+                        const u32x2 a = *reinterpret_cast<const u32x2 *>(tv + v_seg_off(r, 2 * cw + (lg >> 1)) + 8 * (lg & 1));
                         const f32x4 x = mfma16(a, ident, f32x4{0.f, 0.f, 0.f, 0.f});
                         float d[4];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            float f = fvd[4 * it + r];
+                        for (int r2 = 0; r2 < 4; ++r2) {
+                            float f = fvd[4 * it + r2];
                             if (lc != kC) {
-                                const int i = 16 * it + 4 * lg + r;
+                                const int i = 16 * it + 4 * lg + r2;
                                 f = (i < lc) ? lam_pow(l2, lc - 1 - i) : 0.f;
                             }
-                            d[r] = x[r] * f;
+                            d[r2] = x[r2] * f;
                         }
                         const uint32_t x0 = pack_bf16x2(x[0], x[1]), x1 = pack_bf16x2(x[2], x[3]);
                         const u32x2 d01 = split_bf16x2(d[0], d[1]);
@@ -351,30 +373,30 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                     }
 
                     if (kOut) {
-                        // history term Q S^T with S = hi + lo (state before this chunk)
+                        // history term Q S^T with S = hi + lo (state before this chunk); key group s holds
+                        // keys 32s + 8lg .. +7 in tiles 2s (slots 0..3) and 2s+1 (slots 4..7)
                         u32x4 shi[4], slo[4];
 #pragma unroll
-                        for (int kp = 0; kp < 4; ++kp) {
-                            const u32x2 a = split_bf16x2(S[2 * kp][0], S[2 * kp][1]);
-                            const u32x2 b2 = split_bf16x2(S[2 * kp][2], S[2 * kp][3]);
-                            const u32x2 c2 = split_bf16x2(S[2 * kp + 1][0], S[2 * kp + 1][1]);
-                            const u32x2 d2 = split_bf16x2(S[2 * kp + 1][2], S[2 * kp + 1][3]);
-                            shi[kp] = u32x4{a.x, b2.x, c2.x, d2.x};
-                            slo[kp] = u32x4{a.y, b2.y, c2.y, d2.y};
+                        for (int s = 0; s < 4; ++s) {
+                            const u32x2 a = split_bf16x2(S[2 * s][0], S[2 * s][1]);
+                            const u32x2 b2 = split_bf16x2(S[2 * s][2], S[2 * s][3]);
+                            const u32x2 c2 = split_bf16x2(S[2 * s + 1][0], S[2 * s + 1][1]);
+                            const u32x2 d2 = split_bf16x2(S[2 * s + 1][2], S[2 * s + 1][3]);
+                            shi[s] = u32x4{a.x, b2.x, c2.x, d2.x};
+                            slo[s] = u32x4{a.y, b2.y, c2.y, d2.y};
                         }
                         f32x4 acc[4];
 #pragma unroll
                         for (int jt = 0; jt < 4; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int kp = 0; kp < 4; ++kp)
+                        for (int s = 0; s < 4; ++s)
 #pragma unroll
                             for (int jt = 0; jt < 4; ++jt) {
-                                const u32x4 qf = ld_frag_qk(tq, 16 * jt + lr, 32 * kp + 4 * lg);
-                                acc[jt] = mfma32(shi[kp], qf, acc[jt]);
-                                acc[jt] = mfma32(slo[kp], qf, acc[jt]);
+                                const u32x4 qf = ld_row8(tq, 16 * jt + lr, 4 * s + lg);
+                                acc[jt] = mfma32(shi[s], qf, acc[jt]);
+                                acc[jt] = mfma32(slo[s], qf, acc[jt]);
                             }
-                        // within-chunk term P.V, then O = scale (lambda^{j+1} history + within)
-                        const float sc = p.scale;
+                        // O = scale lambda^{j+1} history + P.V (P carries scale)
                         uint16_t *obase = p.o + ((row0 + c0) * p.HV + un.hv) * kDV + v0 + 16 * cw + 4 * lg;
 #pragma unroll
                         for (int jt = 0; jt < 4; ++jt) {
@@ -387,13 +409,13 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                             }
                             const int j = 16 * jt + lr;
                             if (j < lc) {
-                                const u32x2 ov = {pack_bf16x2(sc * a[0], sc * a[1]), pack_bf16x2(sc * a[2], sc * a[3])};
-                                *reinterpret_cast<u32x2 *>(obase + (int64_t)j * v_row_stride) = ov;
+                                const u32x2 ov = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+                                *reinterpret_cast<u32x2 *>(obase + (int64_t)j * (p.HV * kDV)) = ov;
                             }
                         }
                     }
 
-                    // state update S <- lambda^{lc} S + K^T V_dec
+                    // state update S <- lambda^{lc} S + K^T V_dec, K^T fragments read transposed from the K tile
                     const float dec = (lc == kC) ? dec64 : lam_pow(l2, lc);
 #pragma unroll
                     for (int kt = 0; kt < 8; ++kt) S[kt] = S[kt] * dec;
@@ -401,7 +423,10 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                     for (int ip = 0; ip < 2; ++ip)
 #pragma unroll
                         for (int kt = 0; kt < 8; ++kt) {
-                            const u32x4 kf = *reinterpret_cast<const u32x4 *>(ktbuf + ((kt * 2 + ip) * 64 + lane) * 16);
+                            const uint8_t *base = tk + tr_off[kt >> 1] + 8 * (kt & 1) + (32 * ip) * 256;
+                            const u32x2 lo = ld_tr(base);
+                            const u32x2 hi = ld_tr(base + 16 * 256);
+                            const u32x4 kf = u32x4{lo.x, lo.y, hi.x, hi.y};
                             S[kt] = mfma32(kf, vdh[ip], S[kt]);
                             S[kt] = mfma32(kf, vdl[ip], S[kt]);
                         }
@@ -412,101 +437,83 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
             if (slot >= 0 && (p.flags & LA_STATE_WRITE)) {
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt)
-                    *reinterpret_cast<f32x4 *>(plane + vrow * kD + 16 * kt + 4 * lg) = S[kt];
+                    *reinterpret_cast<f32x4 *>(plane + vrow * kD + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1)) = S[kt];
             }
         } else {
-            // ======================================== producer: staging, scores / P, K^T
-            float pf[12];               // score decay factors of this wave's tiles
-            u32x4 pq[4], pk[4], pv[2];  // one chunk of rows in flight
-            const uint16_t *qbase = p.q + (row0 * p.H + h) * kD;
-            const uint16_t *kbase = p.k + (row0 * p.H + h) * kD;
-            const uint16_t *vbase = p.v + (row0 * p.HV + un.hv) * kDV + v0;
-            auto prefetch = [&](int c) {
+            // ======================================== producer: staging and scores / P
+            float pf[16];               // score decay factors (times scale) of this wave's tile block
+            const uint8_t *qseq = reinterpret_cast<const uint8_t *>(p.q + (row0 * p.H + h) * kD);
+            const uint8_t *kseq = reinterpret_cast<const uint8_t *>(p.k + (row0 * p.H + h) * kD);
+            const uint8_t *vseq = reinterpret_cast<const uint8_t *>(p.v + (row0 * p.HV + un.hv) * kDV + v0);
+            // lane -> (row within a 1 KiB block, source segment) for the direct-to-LDS staging loads
+            const int qk_r = lane >> 4, qk_ps = lane & 15;
+            const int v_r = lane >> 3, v_ps = lane & 7;
+            auto stage = [&](int c) {
                 const int c0 = c * kC;
                 const int lc = min(kC, len - c0);
+                uint8_t *tq = smem + kOffQ + (c % 3) * kQKTileB;
+                uint8_t *tk = smem + kOffK + (c % 3) * kQKTileB;
+                uint8_t *tv = smem + kOffV + (c % 3) * kVTileB;
+                // buffer ranges end with the last valid row of the chunk; rows beyond read as zeros
+                const int qk_bytes = (lc - 1) * qk_stride + kD * 2;
+                const int v_bytes = (lc - 1) * v_stride + kVW * 2;
+                const __amdgpu_buffer_rsrc_t rk =
+                    __builtin_amdgcn_make_buffer_rsrc((void *)(kseq + (int64_t)c0 * qk_stride), 0, qk_bytes, kBufDword3);
+                const __amdgpu_buffer_rsrc_t rv =
+                    __builtin_amdgcn_make_buffer_rsrc((void *)(vseq + (int64_t)c0 * v_stride), 0, v_bytes, kBufDword3);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int seg = ptid + 256 * s;
-                    const int r = seg >> 4, col = (seg & 15) * 8;
-                    if (r < lc) {
-                        if (kOut) pq[s] = *reinterpret_cast<const u32x4 *>(qbase + (c0 + r) * qk_row_stride + col);
-                        pk[s] = *reinterpret_cast<const u32x4 *>(kbase + (c0 + r) * qk_row_stride + col);
-                    } else {
-                        pq[s] = u32x4{0, 0, 0, 0};
-                        pk[s] = u32x4{0, 0, 0, 0};
+                for (int b = 0; b < 4; ++b) {
+                    const int blk = 4 * cw + b;                   // 1 KiB block = rows 4blk .. 4blk+3
+                    const int r = 4 * blk + qk_r;
+                    const int off = r * qk_stride + ((qk_ps ^ (r & 15)) << 4);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(tk + blk * 1024), 16, off, 0, 0, 0);
+                }
+                if (kOut) {
+                    const __amdgpu_buffer_rsrc_t rq =
+                        __builtin_amdgcn_make_buffer_rsrc((void *)(qseq + (int64_t)c0 * qk_stride), 0, qk_bytes, kBufDword3);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const int blk = 4 * cw + b;
+                        const int r = 4 * blk + qk_r;
+                        const int off = r * qk_stride + ((qk_ps ^ (r & 15)) << 4);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(tq + blk * 1024), 16, off, 0, 0, 0);
                     }
                 }
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int seg = ptid + 256 * s;
-                    const int r = seg >> 3, col = (seg & 7) * 8;
-                    pv[s] = (r < lc) ? *reinterpret_cast<const u32x4 *>(vbase + (c0 + r) * v_row_stride + col)
-                                     : u32x4{0, 0, 0, 0};
-                }
-            };
-            auto stage = [&](int c) {
-                uint8_t *tq = smem + kOffQ + (c % 3) * kQKTileB;
-                uint8_t *tk = smem + kOffK + (c & 1) * kQKTileB;
-                uint8_t *tv = smem + kOffV + (c % 3) * kVTileB;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int seg = ptid + 256 * s;
-                    const int r = seg >> 4, col = (seg & 15) * 8;
-                    if (kOut) *reinterpret_cast<u32x4 *>(tq + qk_off(r, col)) = pq[s];
-                    *reinterpret_cast<u32x4 *>(tk + qk_off(r, col)) = pk[s];
-                }
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int seg = ptid + 256 * s;
-                    const int r = seg >> 3, col = (seg & 7) * 8;
-                    *reinterpret_cast<u32x4 *>(tv + v_off(r, col)) = pv[s];
+                for (int b = 0; b < 2; ++b) {
+                    const int blk = 2 * cw + b;                   // 1 KiB block = rows 8blk .. 8blk+7
+                    const int r = 8 * blk + v_r;
+                    const int off = r * v_stride + ((v_ps ^ ((r >> 1) & 7)) << 4);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(tv + blk * 1024), 16, off, 0, 0, 0);
                 }
             };
 
             if (kOut) {
                 switch (cw) {
-                case 0: score_factors<0>(pf, l2, lr, lg); break;
-                case 1: score_factors<1>(pf, l2, lr, lg); break;
-                case 2: score_factors<2>(pf, l2, lr, lg); break;
-                default: score_factors<3>(pf, l2, lr, lg); break;
+                case 0: score_factors<0, 2, 2, 1>(pf, l2, p.scale, lr, lg); break;
+                case 1: score_factors<0, 2, 3, 1>(pf, l2, p.scale, lr, lg); break;
+                case 2: score_factors<2, 2, 2, 2>(pf, l2, p.scale, lr, lg); break;
+                default: score_factors<0, 2, 0, 2>(pf, l2, p.scale, lr, lg); break;
                 }
             }
-            if (nch > 0) {
-                prefetch(0);
-                stage(0);
-            }
-            if (nch > 1) prefetch(1);
+            if (nch > 0) stage(0);
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
 
             for (int t = 0; t <= nch; ++t) {
                 if (t + 1 < nch) stage(t + 1);
-                if (t + 2 < nch) prefetch(t + 2);
-                if (t < nch) {
+                if (kOut && t < nch) {
                     const uint8_t *tq = smem + kOffQ + (t % 3) * kQKTileB;
-                    const uint8_t *tk = smem + kOffK + (t & 1) * kQKTileB;
-                    if (kOut) {
-                        uint8_t *pbuf = smem + kOffP + (t & 1) * kPBufB;
-                        switch (cw) {
-                        case 0: produce_scores<0>(pf, tq, tk, pbuf, lane, lr, lg); break;
-                        case 1: produce_scores<1>(pf, tq, tk, pbuf, lane, lr, lg); break;
-                        case 2: produce_scores<2>(pf, tq, tk, pbuf, lane, lr, lg); break;
-                        default: produce_scores<3>(pf, tq, tk, pbuf, lane, lr, lg); break;
-                        }
-                    }
-                    // K^T fragments (exact bf16) for key tiles 2cw, 2cw+1
-                    uint8_t *ktbuf = smem + kOffKT + (t & 1) * kKTBufB;
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        const int kt = 2 * cw + kk;
-#pragma unroll
-                        for (int it = 0; it < 4; ++it) {
-                            const u32x2 a = *reinterpret_cast<const u32x2 *>(tk + qk_off(16 * it + lr, 16 * kt + 4 * lg));
-                            const f32x4 x = mfma16(a, ident, f32x4{0.f, 0.f, 0.f, 0.f});
-                            *reinterpret_cast<u32x2 *>(ktbuf + ((kt * 2 + (it >> 1)) * 64 + lane) * 16 + 8 * (it & 1)) =
-                                u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-                        }
+                    const uint8_t *tk = smem + kOffK + (t % 3) * kQKTileB;
+                    uint8_t *pbuf = smem + kOffP + (t & 1) * kPBufB;
+                    switch (cw) {
+                    case 0: produce_scores<0, 2, 2, 1>(pf, tq, tk, pbuf, lane, lr, lg); break;
+                    case 1: produce_scores<0, 2, 3, 1>(pf, tq, tk, pbuf, lane, lr, lg); break;
+                    case 2: produce_scores<2, 2, 2, 2>(pf, tq, tk, pbuf, lane, lr, lg); break;
+                    default: produce_scores<0, 2, 0, 2>(pf, tq, tk, pbuf, lane, lr, lg); break;
                     }
                 }
+                __builtin_amdgcn_s_waitcnt(0);      // staged rows of chunk t+1 have landed in LDS
                 __syncthreads();
             }
         }
