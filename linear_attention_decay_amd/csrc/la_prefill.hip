@@ -137,22 +137,30 @@ __device__ __forceinline__ Unit decode_unit(int u, const Params &p) {
 // ---------------------------------------------------------------------------------------------------------
 // LDS layout (one workgroup per CU; 144 KiB).
 //   Q, K tiles: 64 rows x 256 B; V tiles (one value half): 64 rows x 128 B. Row-major as in HBM, with the
-//   16-byte segments of row r stored at segment index (seg XOR (r % 16)) for Q/K and (seg XOR ((r/2) % 8))
-//   for V, so that 16-row fragment reads and transposing reads spread over all banks. The tiles are filled
+//   16-byte segments of row r stored at segment index seg XOR (r % 16) for Q, seg XOR f(r % 16) for K
+//   (f swaps the two 2-bit halves of its argument) and seg XOR ((r/2) % 8) for V. LDS serves a 16-byte read
+//   as pairs of 8-lane groups and an 8-byte read as pairs of 16-lane groups, each group within one 128-byte
+//   bank half and the two groups in opposite halves: the Q pattern makes 16-row fragment reads conflict-free;
+//   the K pattern spreads the transposing reads (4 rows x 4 segments per 16 lanes) to the two-way minimum
+//   that a read of one 8-byte half of every segment allows. The tiles are filled
 //   by buffer loads that write LDS directly; the XOR is applied on the source side (lane -> segment), and
 //   rows past the end of a sequence fall outside the buffer range and arrive as zeros.
-//   Q, K, V: 3 buffers each (the consumers read chunk c-1, the producers chunk c, chunk c+1 is in flight).
+//   Q, V: 3 buffers each (the consumers read chunk c-1, the producers chunk c, chunk c+1 is in flight);
+//   K: 2 buffers (only the producers read it).
 //   P: 2 buffers of 6 lower-triangle (jt, token-pair) fragment blocks, hi and lo, 64 lanes x 16 B each.
+//   K^T: 2 buffers of 16 (key tile, token pair) fragment blocks, 64 lanes x 16 B each.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kQKTileB = kC * kD * 2;        // 16384
 constexpr int kVTileB = kC * kVW * 2;        // 8192
 constexpr int kFragB = 64 * 16;              // one fragment block
 constexpr int kPBufB = 6 * 2 * kFragB;       // 12288
+constexpr int kKTBufB = 8 * 2 * kFragB;      // 16384
 constexpr int kOffQ = 0;
 constexpr int kOffK = kOffQ + 3 * kQKTileB;
-constexpr int kOffV = kOffK + 3 * kQKTileB;
+constexpr int kOffV = kOffK + 2 * kQKTileB;
 constexpr int kOffP = kOffV + 3 * kVTileB;
-constexpr int kLdsBytes = kOffP + 2 * kPBufB;
+constexpr int kOffKT = kOffP + 2 * kPBufB;
+constexpr int kLdsBytes = kOffKT + 2 * kKTBufB;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 constexpr int kBufDword3 = 0x00020000;       // buffer resource word 3: raw 32-bit data format
@@ -160,13 +168,14 @@ constexpr int kBufDword3 = 0x00020000;       // buffer resource word 3: raw 32-b
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-__device__ __forceinline__ int qk_seg_off(int r, int seg) { return r * 256 + ((seg ^ (r & 15)) << 4); }
+__device__ __forceinline__ int q_swz(int r) { return r & 15; }
+__device__ __forceinline__ int k_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int q_seg_off(int r, int seg) { return r * 256 + ((seg ^ q_swz(r)) << 4); }
+__device__ __forceinline__ int k_seg_off(int r, int seg) { return r * 256 + ((seg ^ k_swz(r)) << 4); }
 __device__ __forceinline__ int v_seg_off(int r, int seg) { return r * 128 + ((seg ^ ((r >> 1) & 7)) << 4); }
 
-// 8 consecutive elements of a Q/K row: columns 8*seg .. 8*seg+7
-__device__ __forceinline__ u32x4 ld_row8(const uint8_t *tile, int r, int seg) {
-    return *reinterpret_cast<const u32x4 *>(tile + qk_seg_off(r, seg));
-}
+// 8 consecutive elements of a Q or K row: columns 8*seg .. 8*seg+7 (16-byte read)
+__device__ __forceinline__ u32x4 ld16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 // transposing read: see ld_kt_frag
 __device__ __forceinline__ u32x2 ld_tr(const uint8_t *p) {
     const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
@@ -206,32 +215,39 @@ __device__ __forceinline__ void produce_scores(const float (&pf)[16], const uint
     for (int kp = 0; kp < 4; ++kp) {
         u32x4 kf[NI], qf[NJ];
 #pragma unroll
-        for (int x = 0; x < NI; ++x) kf[x] = ld_row8(tk, 16 * (IT0 + x) + lr, 4 * kp + lg);
+        for (int x = 0; x < NI; ++x) kf[x] = ld16(tk + k_seg_off(16 * (IT0 + x) + lr, 4 * kp + lg));
 #pragma unroll
-        for (int x = 0; x < NJ; ++x) qf[x] = ld_row8(tq, 16 * (JT0 + x) + lr, 4 * kp + lg);
+        for (int x = 0; x < NJ; ++x) qf[x] = ld16(tq + q_seg_off(16 * (JT0 + x) + lr, 4 * kp + lg));
 #pragma unroll
         for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
             for (int jj = 0; jj < NJ; ++jj)
                 if (IT0 + ii <= JT0 + jj) a[ii][jj] = mfma32(kf[ii], qf[jj], a[ii][jj]);
     }
+    // every producer block covers whole (jt, token-pair) fragment blocks: NI = 2 with IT0 even, so tiles
+    // (IT0, jt) and (IT0+1, jt) fill the two 8-byte halves of one block (a strictly-upper tile as zeros)
+    static_assert(NI == 2 && (IT0 & 1) == 0, "producer blocks pair token tiles");
 #pragma unroll
-    for (int ii = 0; ii < NI; ++ii)
+    for (int jj = 0; jj < NJ; ++jj) {
+        const int jt = JT0 + jj;
+        uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-            const int it = IT0 + ii, jt = JT0 + jj;
-            uint8_t *dst = pbuf + (p_blk(jt, it >> 1) * 2) * kFragB + lane * 16 + 8 * (it & 1);
+        for (int ii = 0; ii < 2; ++ii) {
+            const int it = IT0 + ii;
             if (it <= jt) {
                 const float *f = &pf[4 * (NJ * ii + jj)];
                 const u32x2 a01 = split_bf16x2(a[ii][jj][0] * f[0], a[ii][jj][1] * f[1]);
                 const u32x2 a23 = split_bf16x2(a[ii][jj][2] * f[2], a[ii][jj][3] * f[3]);
-                *reinterpret_cast<u32x2 *>(dst) = u32x2{a01.x, a23.x};
-                *reinterpret_cast<u32x2 *>(dst + kFragB) = u32x2{a01.y, a23.y};
-            } else if (it == jt + 1 && (jt & 1) == 0) {
-                *reinterpret_cast<u32x2 *>(dst) = u32x2{0, 0};
-                *reinterpret_cast<u32x2 *>(dst + kFragB) = u32x2{0, 0};
+                hi[2 * ii] = a01.x; hi[2 * ii + 1] = a23.x;
+                lo[2 * ii] = a01.y; lo[2 * ii + 1] = a23.y;
+            } else {
+                hi[2 * ii] = hi[2 * ii + 1] = lo[2 * ii] = lo[2 * ii + 1] = 0u;
             }
         }
+        uint8_t *dst = pbuf + (p_blk(jt, IT0 >> 1) * 2) * kFragB + lane * 16;
+        *reinterpret_cast<u32x4 *>(dst) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        *reinterpret_cast<u32x4 *>(dst + kFragB) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
 }
 
 // ---------------------------------------------------------------------------------------------------------
@@ -299,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
             // ======================================== consumer: owns the state rows of value tile cw
             // State tiles S[kt] (kt = 0..7), lane holds S[v][k] for v = v0 + 16cw + lr and the four keys
             // k = kappa(kt, 4lg + r) = 32(kt/2) + 8lg + 4(kt%2) + r, r = 0..3: the key order inside a tile is
-            // chosen (through the transposing K reads below) so that tiles 2s and 2s+1 together give each lane
+            // chosen (through the transposing K reads that build the K^T fragments) so that tiles 2s and 2s+1 give each lane
             // 8 consecutive keys -- the slot layout of a plain 16-byte Q row read.
             f32x4 S[8];
             float fvd[16];              // lambda^{63-i} for i = 16it+4lg+r (full chunk)
@@ -322,45 +338,81 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
             s16x4 ident;
 #pragma unroll
             for (int e = 0; e < 4; ++e) ident[e] = (4 * lg + e == lr) ? (short)0x3F80 : (short)0;
-            // transposing K reads: source lane (lg, lr) supplies row 4lg + lr/4 (+ token-pair and half
-            // offsets) and the 4 keys 32s + 8(lr%4) + 4(kt%2) .. +3; the instruction hands lane lr of each
-            // 16-lane group key kappa(kt, lr) of the 4 rows of its group.
-            const int tr_row = 4 * lg + (lr >> 2);
-            int tr_off[4];
+            // per-lane LDS offsets reused by every chunk: Q fragment (row lr, segment 4s + lg; row tile jt adds
+            // 4096 B), V^T source (row lr, value tile cw; token tile it adds 2048 B)
+            int q_off[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) tr_off[s] = qk_seg_off(tr_row, 4 * s + (lr & 3));
+            for (int s = 0; s < 4; ++s) q_off[s] = q_seg_off(lr, 4 * s + lg);
+            const int v_off = v_seg_off(lr, 2 * cw + (lg >> 1)) + 8 * (lg & 1);
+            // K^T fragments for key tiles 2cw, 2cw+1 (kt = 2s + kk with s = cw): transposing reads. Source lane
+            // (lg, lr) supplies token row 4lg + lr/4 (+ 32 per token pair, + 16 for slots 4..7) and the 4 keys
+            // 32s + 8(lr%4) + 4kk .. +3; the instruction hands lane lr of each 16-lane group key kappa(kt, lr)
+            // = 32s + 8(lr/4) + 4kk + lr%4 of the 4 rows of its group.
+            const int tr_off = k_seg_off(4 * lg + (lr >> 2), 4 * cw + (lr & 3));
             __syncthreads();
 
             for (int t = 0; t <= nch; ++t) {
+                if (t < nch) {
+                    const uint8_t *tk = smem + kOffK + (t & 1) * kQKTileB;
+                    uint8_t *ktbuf = smem + kOffKT + (t & 1) * kKTBufB + lane * 16;
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int ip = 0; ip < 2; ++ip) {
+                            const uint8_t *src = tk + tr_off + 8 * kk + (32 * ip) * 256;
+                            const u32x2 lo = ld_tr(src);
+                            const u32x2 hi = ld_tr(src + 16 * 256);
+                            *reinterpret_cast<u32x4 *>(ktbuf + ((2 * cw + kk) * 2 + ip) * kFragB) =
+                                u32x4{lo.x, lo.y, hi.x, hi.y};
+                        }
+                }
                 if (t > 0) {
                     const int c = t - 1;
                     const int c0 = c * kC;
                     const int lc = min(kC, len - c0);
                     const uint8_t *tq = smem + kOffQ + (c % 3) * kQKTileB;
-                    const uint8_t *tk = smem + kOffK + (c % 3) * kQKTileB;
                     const uint8_t *tv = smem + kOffV + (c % 3) * kVTileB;
                     const uint8_t *pbuf = smem + kOffP + (c & 1) * kPBufB;
+                    const uint8_t *ktbuf = smem + kOffKT + (c & 1) * kKTBufB + lane * 16;
+
+                    // a short last chunk: decay factors for its own length (every exponent stays >= 0)
+                    if (lc != kC) {
+#pragma unroll
+                        for (int it = 0; it < 4; ++it)
+#pragma unroll
+                            for (int r2 = 0; r2 < 4; ++r2) {
+                                const int i = 16 * it + 4 * lg + r2;
+                                fvd[4 * it + r2] = (i < lc) ? lam_pow(l2, lc - 1 - i) : 0.f;
+                            }
+                    }
+                    const float dec = (lc == kC) ? dec64 : lam_pow(l2, lc);
+
+                    // the state before this chunk as bf16 hi + lo for the history term Q S^T; key group s holds
+                    // keys 32s + 8lg .. +7 in tiles 2s (slots 0..3) and 2s+1 (slots 4..7)
+                    u32x4 shi[4], slo[4];
+                    if (kOut) {
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            const u32x2 a = split_bf16x2(S[2 * s][0], S[2 * s][1]);
+                            const u32x2 b2 = split_bf16x2(S[2 * s][2], S[2 * s][3]);
+                            const u32x2 c2 = split_bf16x2(S[2 * s + 1][0], S[2 * s + 1][1]);
+                            const u32x2 d2 = split_bf16x2(S[2 * s + 1][2], S[2 * s + 1][3]);
+                            shi[s] = u32x4{a.x, b2.x, c2.x, d2.x};
+                            slo[s] = u32x4{a.y, b2.y, c2.y, d2.y};
+                        }
+                    }
+#pragma unroll
+                    for (int kt = 0; kt < 8; ++kt) S[kt] = S[kt] * dec;
 
                     // V^T fragments of this wave's value tile, and V_dec = lambda^{lc-1-i} v_i as hi + lo
                     u32x4 vf[2], vdh[2], vdl[2];
 #pragma unroll
                     for (int it = 0; it < 4; ++it) {
-                        const int r = 16 * it + lr;
-                        const u32x2 a = *reinterpret_cast<const u32x2 *>(tv + v_seg_off(r, 2 * cw + (lg >> 1)) + 8 * (lg & 1));
+                        const u32x2 a = *reinterpret_cast<const u32x2 *>(tv + v_off + 2048 * it);
                         const f32x4 x = mfma16(a, ident, f32x4{0.f, 0.f, 0.f, 0.f});
-                        float d[4];
-#pragma unroll
-                        for (int r2 = 0; r2 < 4; ++r2) {
-                            float f = fvd[4 * it + r2];
-                            if (lc != kC) {
-                                const int i = 16 * it + 4 * lg + r2;
-                                f = (i < lc) ? lam_pow(l2, lc - 1 - i) : 0.f;
-                            }
-                            d[r2] = x[r2] * f;
-                        }
                         const uint32_t x0 = pack_bf16x2(x[0], x[1]), x1 = pack_bf16x2(x[2], x[3]);
-                        const u32x2 d01 = split_bf16x2(d[0], d[1]);
-                        const u32x2 d23 = split_bf16x2(d[2], d[3]);
+                        const u32x2 d01 = split_bf16x2(x[0] * fvd[4 * it + 0], x[1] * fvd[4 * it + 1]);
+                        const u32x2 d23 = split_bf16x2(x[2] * fvd[4 * it + 2], x[3] * fvd[4 * it + 3]);
                         if ((it & 1) == 0) {
                             vf[it >> 1].x = x0; vf[it >> 1].y = x1;
                             vdh[it >> 1].x = d01.x; vdh[it >> 1].y = d23.x;
@@ -372,32 +424,39 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                         }
                     }
 
-                    if (kOut) {
-                        // history term Q S^T with S = hi + lo (state before this chunk); key group s holds
-                        // keys 32s + 8lg .. +7 in tiles 2s (slots 0..3) and 2s+1 (slots 4..7)
-                        u32x4 shi[4], slo[4];
+                    // history term (acc) and state update S <- lambda^{lc} S + K^T V_dec, interleaved per key
+                    // group
+                    f32x4 acc[4];
 #pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            const u32x2 a = split_bf16x2(S[2 * s][0], S[2 * s][1]);
-                            const u32x2 b2 = split_bf16x2(S[2 * s][2], S[2 * s][3]);
-                            const u32x2 c2 = split_bf16x2(S[2 * s + 1][0], S[2 * s + 1][1]);
-                            const u32x2 d2 = split_bf16x2(S[2 * s + 1][2], S[2 * s + 1][3]);
-                            shi[s] = u32x4{a.x, b2.x, c2.x, d2.x};
-                            slo[s] = u32x4{a.y, b2.y, c2.y, d2.y};
-                        }
-                        f32x4 acc[4];
+                    for (int jt = 0; jt < 4; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int jt = 0; jt < 4; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int s = 0; s < 4; ++s)
+                    for (int s = 0; s < 4; ++s) {
+                        if (kOut) {
 #pragma unroll
                             for (int jt = 0; jt < 4; ++jt) {
-                                const u32x4 qf = ld_row8(tq, 16 * jt + lr, 4 * s + lg);
+                                const u32x4 qf = ld16(tq + q_off[s] + 4096 * jt);
                                 acc[jt] = mfma32(shi[s], qf, acc[jt]);
                                 acc[jt] = mfma32(slo[s], qf, acc[jt]);
                             }
-                        // O = scale lambda^{j+1} history + P.V (P carries scale)
-                        uint16_t *obase = p.o + ((row0 + c0) * p.HV + un.hv) * kDV + v0 + 16 * cw + 4 * lg;
+                        }
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) {
+                            const int kt = 2 * s + kk;
+#pragma unroll
+                            for (int ip = 0; ip < 2; ++ip) {
+                                const u32x4 kf = ld16(ktbuf + (kt * 2 + ip) * kFragB);
+                                S[kt] = mfma32(kf, vdh[ip], S[kt]);
+                                S[kt] = mfma32(kf, vdl[ip], S[kt]);
+                            }
+                        }
+                    }
+
+                    if (kOut) {
+                        // O = scale lambda^{j+1} history + P.V (P carries scale); rows j >= lc fall outside the
+                        // buffer range of the store and are dropped
+                        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+                            (void *)(p.o + ((row0 + c0) * p.HV + un.hv) * kDV + v0 + 16 * cw), 0,
+                            (lc - 1) * p.HV * kDV * 2 + 32, kBufDword3);
 #pragma unroll
                         for (int jt = 0; jt < 4; ++jt) {
                             f32x4 a = acc[jt] * finter[jt];
@@ -408,28 +467,10 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                                 a = mfma32(vf[ip], *reinterpret_cast<const u32x4 *>(blk + kFragB), a);
                             }
                             const int j = 16 * jt + lr;
-                            if (j < lc) {
-                                const u32x2 ov = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-                                *reinterpret_cast<u32x2 *>(obase + (int64_t)j * (p.HV * kDV)) = ov;
-                            }
+                            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])},
+                                                                  ro, j * (p.HV * kDV * 2) + 8 * lg, 0, 0);
                         }
                     }
-
-                    // state update S <- lambda^{lc} S + K^T V_dec, K^T fragments read transposed from the K tile
-                    const float dec = (lc == kC) ? dec64 : lam_pow(l2, lc);
-#pragma unroll
-                    for (int kt = 0; kt < 8; ++kt) S[kt] = S[kt] * dec;
-#pragma unroll
-                    for (int ip = 0; ip < 2; ++ip)
-#pragma unroll
-                        for (int kt = 0; kt < 8; ++kt) {
-                            const uint8_t *base = tk + tr_off[kt >> 1] + 8 * (kt & 1) + (32 * ip) * 256;
-                            const u32x2 lo = ld_tr(base);
-                            const u32x2 hi = ld_tr(base + 16 * 256);
-                            const u32x4 kf = u32x4{lo.x, lo.y, hi.x, hi.y};
-                            S[kt] = mfma32(kf, vdh[ip], S[kt]);
-                            S[kt] = mfma32(kf, vdl[ip], S[kt]);
-                        }
                 }
                 __syncthreads();
             }
@@ -445,14 +486,26 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
             const uint8_t *qseq = reinterpret_cast<const uint8_t *>(p.q + (row0 * p.H + h) * kD);
             const uint8_t *kseq = reinterpret_cast<const uint8_t *>(p.k + (row0 * p.H + h) * kD);
             const uint8_t *vseq = reinterpret_cast<const uint8_t *>(p.v + (row0 * p.HV + un.hv) * kDV + v0);
-            // lane -> (row within a 1 KiB block, source segment) for the direct-to-LDS staging loads
-            const int qk_r = lane >> 4, qk_ps = lane & 15;
-            const int v_r = lane >> 3, v_ps = lane & 7;
+            // per-lane source offsets of the direct-to-LDS staging loads (the same for every chunk): Q/K
+            // block b of this producer holds rows 4(4cw+b) .. +3, lane -> (row 4(4cw+b) + lane/16, physical
+            // segment lane%16); V block b holds rows 8(2cw+b) .. +7, lane -> (row + lane/8, segment lane%8)
+            int q_src[4], k_src[4], v_src[2];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int r = 4 * (4 * cw + b) + (lane >> 4);
+                q_src[b] = r * qk_stride + (((lane & 15) ^ q_swz(r)) << 4);
+                k_src[b] = r * qk_stride + (((lane & 15) ^ k_swz(r)) << 4);
+            }
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int r = 8 * (2 * cw + b) + (lane >> 3);
+                v_src[b] = r * v_stride + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+            }
             auto stage = [&](int c) {
                 const int c0 = c * kC;
                 const int lc = min(kC, len - c0);
                 uint8_t *tq = smem + kOffQ + (c % 3) * kQKTileB;
-                uint8_t *tk = smem + kOffK + (c % 3) * kQKTileB;
+                uint8_t *tk = smem + kOffK + (c & 1) * kQKTileB;
                 uint8_t *tv = smem + kOffV + (c % 3) * kVTileB;
                 // buffer ranges end with the last valid row of the chunk; rows beyond read as zeros
                 const int qk_bytes = (lc - 1) * qk_stride + kD * 2;
@@ -462,30 +515,18 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                 const __amdgpu_buffer_rsrc_t rv =
                     __builtin_amdgcn_make_buffer_rsrc((void *)(vseq + (int64_t)c0 * v_stride), 0, v_bytes, kBufDword3);
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int blk = 4 * cw + b;                   // 1 KiB block = rows 4blk .. 4blk+3
-                    const int r = 4 * blk + qk_r;
-                    const int off = r * qk_stride + ((qk_ps ^ (r & 15)) << 4);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(tk + blk * 1024), 16, off, 0, 0, 0);
-                }
+                for (int b = 0; b < 4; ++b)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(tk + (4 * cw + b) * 1024), 16, k_src[b], 0, 0, 0);
                 if (kOut) {
                     const __amdgpu_buffer_rsrc_t rq =
                         __builtin_amdgcn_make_buffer_rsrc((void *)(qseq + (int64_t)c0 * qk_stride), 0, qk_bytes, kBufDword3);
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const int blk = 4 * cw + b;
-                        const int r = 4 * blk + qk_r;
-                        const int off = r * qk_stride + ((qk_ps ^ (r & 15)) << 4);
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(tq + blk * 1024), 16, off, 0, 0, 0);
-                    }
+                    for (int b = 0; b < 4; ++b)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(tq + (4 * cw + b) * 1024), 16, q_src[b], 0, 0, 0);
                 }
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    const int blk = 2 * cw + b;                   // 1 KiB block = rows 8blk .. 8blk+7
-                    const int r = 8 * blk + v_r;
-                    const int off = r * v_stride + ((v_ps ^ ((r >> 1) & 7)) << 4);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(tv + blk * 1024), 16, off, 0, 0, 0);
-                }
+                for (int b = 0; b < 2; ++b)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(tv + (2 * cw + b) * 1024), 16, v_src[b], 0, 0, 0);
             };
 
             if (kOut) {
@@ -504,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                 if (t + 1 < nch) stage(t + 1);
                 if (kOut && t < nch) {
                     const uint8_t *tq = smem + kOffQ + (t % 3) * kQKTileB;
-                    const uint8_t *tk = smem + kOffK + (t % 3) * kQKTileB;
+                    const uint8_t *tk = smem + kOffK + (t & 1) * kQKTileB;
                     uint8_t *pbuf = smem + kOffP + (t & 1) * kPBufB;
                     switch (cw) {
                     case 0: produce_scores<0, 2, 2, 1>(pf, tq, tk, pbuf, lane, lr, lg); break;
