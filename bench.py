@@ -53,6 +53,26 @@ def mfma_flops_executed(w):
     return per_chunk_head * chunks * w.HV
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "la_chunk_kernel_fixed_b2_t8192_h64_hbm_traffic.md")
+KERNEL_SRC = os.path.join(ROOT, "linear_attention_decay_amd", "csrc", "la_prefill.hip")
+
+
+def measured_traffic(config):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary, if it was taken on this kernel
+    source and this workload; else None."""
+    import hashlib
+    if config != 1 or not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if f"Kernel source sha256: {sha}" not in txt:
+        return None
+    for line in txt.splitlines():
+        if line.startswith("traffic_bytes_per_launch:"):
+            return int(line.split(":")[1])
+    return None
+
+
 def cpu_baseline(w, max_units=None):
     """Time the FP64 oracle on a bounded sample of the same workload: whole (sequence, value head) units."""
     import numpy as np
@@ -192,7 +212,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "HV": w.HV, "D": 128, "DV": 128,
                    "chunk": CHUNK, "state_flags": w.flags, "tokens": w.tokens},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
                      "kernel": "la_chunk_kernel<0>", "kernel_ms_avg": round(kern_ms, 6),
                      "kernel_ms_median": round(per[len(per) // 2], 6), "algorithmic_bytes": alg_bytes},
         "mfma": {"executed_tflops": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
