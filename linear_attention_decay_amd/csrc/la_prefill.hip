@@ -9,9 +9,10 @@
 //     O_j = scale * ( sum_{i<=j} lambda^{j-i} (q_j . k_i) v_i  +  lambda^{j+1} S q_j )
 //     S  <- lambda^{Lc} S + sum_i k_i (lambda^{Lc-1-i} v_i)^T      (kept as S^T[k][v] on chip)
 //
-// Work decomposition: one workgroup = (sequence, value head, half of the 128 value columns). 4 wave64s;
-// wave w owns value columns [16w, 16w+16) of its half: the state rows S[v][0..127] for those columns stay in
-// that wave's registers as MFMA accumulators for the whole sequence.
+// Work decomposition: one workgroup = (sequence, value head, half of the 128 value columns), 8 wave64s. The 4
+// consumer waves each own value columns [16w, 16w+16) of the half: the state rows S[v][0..127] for those
+// columns stay in that wave's registers as MFMA accumulators for the whole sequence. The 4 producer waves
+// stage Q, K, V tiles into LDS and compute the decay-masked intra-chunk scores.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16, FP32 accumulate). Every operand fragment a lane holds is
 // "row r = lane % 16, slot group g = lane / 16, 8 slots"; slots 0..3 carry contraction indices 4g..4g+3 of
@@ -31,6 +32,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <stdio.h>
 #include <stdarg.h>
 #include <string.h>
@@ -87,14 +89,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     bf16x2 h = __builtin_convertvector(f, bf16x2);   // v_cvt_pk_bf16_f32, round to nearest even
     return __builtin_bit_cast(uint32_t, h);
 }
-__device__ __forceinline__ float lo_bf16_as_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float hi_bf16_as_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
 // x = hi + lo with hi = bf16(x), lo = bf16(x - hi); two values per call, returned as {hi pair, lo pair}.
+// The residual x - hi is exact in FP32; it is formed by one bf16 dot product against (-1, 0) or (0, -1)
+// accumulated onto x. The two masks are passed in registers: given the pair (-1, 0) as a constant, the
+// compiler encodes it as the inline constant -1.0, which the hardware reads as the FP32 bit pattern
+// 0xBF800000, i.e. the pair (0, -1).
 __device__ __forceinline__ u32x2 split_bf16x2(float a, float b) {
-    const uint32_t hi = pack_bf16x2(a, b);
-    const uint32_t lo = pack_bf16x2(a - lo_bf16_as_f32(hi), b - hi_bf16_as_f32(hi));
-    return u32x2{hi, lo};
+    f32x2 f = {a, b};
+    const bf16x2 hi = __builtin_convertvector(f, bf16x2);
+    uint32_t m0 = 0x0000BF80u, m1 = 0xBF800000u;     // bf16 pairs (-1, 0) and (0, -1), element 0 low
+    asm("" : "+v"(m0), "+v"(m1));
+    const float ra = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, m0), a, false);
+    const float rb = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, m1), b, false);
+    return u32x2{__builtin_bit_cast(uint32_t, hi), pack_bf16x2(ra, rb)};
 }
 
 __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
@@ -145,22 +153,24 @@ __device__ __forceinline__ Unit decode_unit(int u, const Params &p) {
 //   that a read of one 8-byte half of every segment allows. The tiles are filled
 //   by buffer loads that write LDS directly; the XOR is applied on the source side (lane -> segment), and
 //   rows past the end of a sequence fall outside the buffer range and arrive as zeros.
-//   Q, V: 3 buffers each (the consumers read chunk c-1, the producers chunk c, chunk c+1 is in flight);
-//   K: 2 buffers (only the producers read it).
-//   P: 2 buffers of 6 lower-triangle (jt, token-pair) fragment blocks, hi and lo, 64 lanes x 16 B each.
-//   K^T: 2 buffers of 16 (key tile, token pair) fragment blocks, 64 lanes x 16 B each.
+//   Q, K, V: 3 buffers each. In the iteration that handles chunk c, both roles read chunk c's tiles, chunk
+//   c+1 has landed and chunk c+2 is in flight.
+//   P: 2 buffers of 6 lower-triangle (jt, token-pair) fragment blocks, hi and lo, 64 lanes x 16 B each:
+//   written for chunk c by the producers while the consumers read chunk c-1's.
+//   O: 2 buffers of one output tile (64 rows x 128 B, bf16, swizzled like V): the consumers write chunk c-1's
+//   output in iteration c; the producers store it to HBM in iteration c+1 as whole 128-byte row halves.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kQKTileB = kC * kD * 2;        // 16384
 constexpr int kVTileB = kC * kVW * 2;        // 8192
 constexpr int kFragB = 64 * 16;              // one fragment block
 constexpr int kPBufB = 6 * 2 * kFragB;       // 12288
-constexpr int kKTBufB = 8 * 2 * kFragB;      // 16384
 constexpr int kOffQ = 0;
 constexpr int kOffK = kOffQ + 3 * kQKTileB;
-constexpr int kOffV = kOffK + 2 * kQKTileB;
+constexpr int kOffV = kOffK + 3 * kQKTileB;
 constexpr int kOffP = kOffV + 3 * kVTileB;
-constexpr int kOffKT = kOffP + 2 * kPBufB;
-constexpr int kLdsBytes = kOffKT + 2 * kKTBufB;
+constexpr int kOTileB = kC * kVW * 2;        // 8192
+constexpr int kOffO = kOffP + 2 * kPBufB;
+constexpr int kLdsBytes = kOffO + 2 * kOTileB;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 constexpr int kBufDword3 = 0x00020000;       // buffer resource word 3: raw 32-bit data format
@@ -176,7 +186,8 @@ __device__ __forceinline__ int v_seg_off(int r, int seg) { return r * 128 + ((se
 
 // 8 consecutive elements of a Q or K row: columns 8*seg .. 8*seg+7 (16-byte read)
 __device__ __forceinline__ u32x4 ld16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
-// transposing read: see ld_kt_frag
+// transposing read (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element i % 4 of the 8 bytes
+// that lane 4e + i / 4 addresses, as its element e
 __device__ __forceinline__ u32x2 ld_tr(const uint8_t *p) {
     const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
     return __builtin_bit_cast(u32x2, x);
@@ -251,11 +262,29 @@ __device__ __forceinline__ void produce_scores(const float (&pf)[16], const uint
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// the kernel: 8 waves; waves 0..3 are consumers (state owners), waves 4..7 producers
+// the kernel: 8 waves; waves 0..3 are consumers (state owners), waves 4..7 producers.
+//
+// Iteration c (one workgroup barrier at its end): the producers issue the staging loads of chunk c+2 and
+// compute chunk c's decay-masked scores P; the consumers finish chunk c-1's output (P of chunk c-1 from the
+// previous iteration, its history term from registers) and take chunk c's history term Q S^T and state
+// update. The producers wait only for chunk c+1's loads before the barrier, so two chunks of loads overlap
+// the compute.
 // ---------------------------------------------------------------------------------------------------------
+struct FullChunk { static constexpr bool kTail = false; };
+struct TailChunk { static constexpr bool kTail = true; };
+
+// s_waitcnt with vmcnt(N), lgkmcnt(0) and no expcnt wait (gfx9 encoding: vmcnt bits [3:0] and [15:14],
+// expcnt [6:4], lgkmcnt [11:8])
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
     constexpr bool kOut = (MODE != kCommit);
+    constexpr int kStageLoads = kOut ? 10 : 6;       // buffer loads one producer wave issues per chunk
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
 
     const int tid = threadIdx.x;
@@ -303,23 +332,23 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
         float l2 = -p.slope[un.hv] * 1.4426950408889634f;
         l2 = fmaxf(l2, -1.0e30f);                                    // slope = +inf -> lambda^0 = 1, lambda^n = 0
         const int nch = (len + kC - 1) / kC;
-        const float dec64 = lam_pow(l2, kC);
         const int qk_stride = p.H * kD * 2;                          // bytes between token rows
         const int v_stride = p.HV * kDV * 2;
         float *plane = nullptr;
         if (slot >= 0) plane = p.pool + ((int64_t)slot * p.HV + un.hv) * (kDV * kD);
 
-        // The two roles run separate loops with the same number of workgroup barriers (one before the chunk
-        // loop, one per iteration), so each role's loop-carried registers are allocated on their own.
+        // The two roles run separate code with the same number of workgroup barriers (nch + 2 per unit), so
+        // each role's loop-carried registers are allocated on their own.
         if (consumer) {
             // ======================================== consumer: owns the state rows of value tile cw
             // State tiles S[kt] (kt = 0..7), lane holds S[v][k] for v = v0 + 16cw + lr and the four keys
             // k = kappa(kt, 4lg + r) = 32(kt/2) + 8lg + 4(kt%2) + r, r = 0..3: the key order inside a tile is
-            // chosen (through the transposing K reads that build the K^T fragments) so that tiles 2s and 2s+1 give each lane
-            // 8 consecutive keys -- the slot layout of a plain 16-byte Q row read.
+            // chosen (through the transposing K reads that build the K^T fragments) so that tiles 2s and 2s+1
+            // give each lane 8 consecutive keys -- the slot layout of a plain 16-byte Q row read.
             f32x4 S[8];
-            float fvd[16];              // lambda^{63-i} for i = 16it+4lg+r (full chunk)
+            float fvd64[16];            // lambda^{63-i} for i = 16it+4lg+r (full chunk)
             float finter[4];            // scale lambda^{j+1} for j = 16jt+lr
+            const float dec64 = lam_pow(l2, kC);
             const int vrow = v0 + 16 * cw + lr;
             if (slot >= 0 && (p.flags & LA_STATE_READ)) {
 #pragma unroll
@@ -332,145 +361,222 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
 #pragma unroll
             for (int it = 0; it < 4; ++it)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) fvd[4 * it + r] = lam_pow(l2, 63 - (16 * it + 4 * lg + r));
+                for (int r = 0; r < 4; ++r) fvd64[4 * it + r] = lam_pow(l2, 63 - (16 * it + 4 * lg + r));
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) finter[jt] = p.scale * lam_pow(l2, 16 * jt + lr + 1);
             s16x4 ident;
 #pragma unroll
             for (int e = 0; e < 4; ++e) ident[e] = (4 * lg + e == lr) ? (short)0x3F80 : (short)0;
             // per-lane LDS offsets reused by every chunk: Q fragment (row lr, segment 4s + lg; row tile jt adds
-            // 4096 B), V^T source (row lr, value tile cw; token tile it adds 2048 B)
-            int q_off[4];
+            // 4096 B); V^T source (row lr, value tile cw; token tile it adds 2048 B); K^T source of key group s:
+            // lane (lg, lr) supplies token row 4lg + lr/4 (+ 32 per token pair, + 16 for slots 4..7) and the 4
+            // keys 32s + 8(lr%4) + 4kk .. +3; the transposing read hands lane lr of each 16-lane group key
+            // kappa(2s + kk, lr) = 32s + 8(lr/4) + 4kk + lr%4 of the 4 rows of its group.
+            int q_off[4], tr_off[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) q_off[s] = q_seg_off(lr, 4 * s + lg);
+            for (int s = 0; s < 4; ++s) {
+                q_off[s] = q_seg_off(lr, 4 * s + lg);
+                tr_off[s] = k_seg_off(4 * lg + (lr >> 2), 4 * s + (lr & 3));
+            }
             const int v_off = v_seg_off(lr, 2 * cw + (lg >> 1)) + 8 * (lg & 1);
-            // K^T fragments for key tiles 2cw, 2cw+1 (kt = 2s + kk with s = cw): transposing reads. Source lane
-            // (lg, lr) supplies token row 4lg + lr/4 (+ 32 per token pair, + 16 for slots 4..7) and the 4 keys
-            // 32s + 8(lr%4) + 4kk .. +3; the instruction hands lane lr of each 16-lane group key kappa(kt, lr)
-            // = 32s + 8(lr/4) + 4kk + lr%4 of the 4 rows of its group.
-            const int tr_off = k_seg_off(4 * lg + (lr >> 2), 4 * cw + (lr & 3));
-            __syncthreads();
 
-            for (int t = 0; t <= nch; ++t) {
-                if (t < nch) {
-                    const uint8_t *tk = smem + kOffK + (t & 1) * kQKTileB;
-                    uint8_t *ktbuf = smem + kOffKT + (t & 1) * kKTBufB + lane * 16;
+            // Carried from the iteration that takes chunk c's history term to the one that writes its output:
+            // the history term (acc) and chunk c's V^T fragments (vf).
+            f32x4 acc[4];
 #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk)
+            for (int jt = 0; jt < 4; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            u32x4 vf[2];
+            vf[0] = vf[1] = u32x4{0u, 0u, 0u, 0u};
+
+            // V_dec factors lambda^{lc-1-i} of a chunk of lc tokens; the factors of missing rows are zero and
+            // every exponent handed to exp2 stays >= 0
+            auto tail_factors = [&](int lc, float (&fvd)[16]) {
 #pragma unroll
-                        for (int ip = 0; ip < 2; ++ip) {
-                            const uint8_t *src = tk + tr_off + 8 * kk + (32 * ip) * 256;
-                            const u32x2 lo = ld_tr(src);
-                            const u32x2 hi = ld_tr(src + 16 * 256);
-                            *reinterpret_cast<u32x4 *>(ktbuf + ((2 * cw + kk) * 2 + ip) * kFragB) =
-                                u32x4{lo.x, lo.y, hi.x, hi.y};
-                        }
+                for (int it = 0; it < 4; ++it)
+#pragma unroll
+                    for (int r2 = 0; r2 < 4; ++r2) {
+                        const int i = 16 * it + 4 * lg + r2;
+                        fvd[4 * it + r2] = (i < lc) ? lam_pow(l2, lc - 1 - i) : 0.f;
+                    }
+            };
+            // V fragments from the 8 raw bytes `a` of token tile it: V^T (exact, through the identity MFMA)
+            // and V_dec = lambda^{lc-1-i} v_i as bf16 hi + lo
+            auto prep_part = [&](u32x2 a, int it, const float (&fvd)[16], u32x4 (&vdh)[2], u32x4 (&vdl)[2]) {
+                const f32x4 x = mfma16(a, ident, f32x4{0.f, 0.f, 0.f, 0.f});
+                const uint32_t x0 = pack_bf16x2(x[0], x[1]), x1 = pack_bf16x2(x[2], x[3]);
+                const u32x2 d01 = split_bf16x2(x[0] * fvd[4 * it + 0], x[1] * fvd[4 * it + 1]);
+                const u32x2 d23 = split_bf16x2(x[2] * fvd[4 * it + 2], x[3] * fvd[4 * it + 3]);
+                if ((it & 1) == 0) {
+                    vf[it >> 1].x = x0; vf[it >> 1].y = x1;
+                    vdh[it >> 1].x = d01.x; vdh[it >> 1].y = d23.x;
+                    vdl[it >> 1].x = d01.y; vdl[it >> 1].y = d23.y;
+                } else {
+                    vf[it >> 1].z = x0; vf[it >> 1].w = x1;
+                    vdh[it >> 1].z = d01.x; vdh[it >> 1].w = d23.x;
+                    vdl[it >> 1].z = d01.y; vdl[it >> 1].w = d23.y;
                 }
-                if (t > 0) {
-                    const int c = t - 1;
-                    const int c0 = c * kC;
-                    const int lc = min(kC, len - c0);
-                    const uint8_t *tq = smem + kOffQ + (c % 3) * kQKTileB;
-                    const uint8_t *tv = smem + kOffV + (c % 3) * kVTileB;
-                    const uint8_t *pbuf = smem + kOffP + (c & 1) * kPBufB;
-                    const uint8_t *ktbuf = smem + kOffKT + (c & 1) * kKTBufB + lane * 16;
-
-                    // a short last chunk: decay factors for its own length (every exponent stays >= 0)
-                    if (lc != kC) {
+            };
+            auto load_v = [&](int c, u32x2 (&va)[4]) {
+                const uint8_t *tv = smem + kOffV + (c % 3) * kVTileB + v_off;
 #pragma unroll
-                        for (int it = 0; it < 4; ++it)
+                for (int it = 0; it < 4; ++it) va[it] = *reinterpret_cast<const u32x2 *>(tv + 2048 * it);
+            };
+            // the state before the chunk as bf16 hi + lo for the history term (key group s: keys 32s + 8lg .. +7
+            // in tiles 2s, slots 0..3, and 2s+1, slots 4..7), then the decay of those two tiles
+            auto split_dec = [&](int s, float dec, u32x4 &shi, u32x4 &slo) {
+                if (kOut) {
+                    const u32x2 a = split_bf16x2(S[2 * s][0], S[2 * s][1]);
+                    const u32x2 b2 = split_bf16x2(S[2 * s][2], S[2 * s][3]);
+                    const u32x2 c2 = split_bf16x2(S[2 * s + 1][0], S[2 * s + 1][1]);
+                    const u32x2 d2 = split_bf16x2(S[2 * s + 1][2], S[2 * s + 1][3]);
+                    shi = u32x4{a.x, b2.x, c2.x, d2.x};
+                    slo = u32x4{a.y, b2.y, c2.y, d2.y};
+                }
+                S[2 * s] = S[2 * s] * dec;
+                S[2 * s + 1] = S[2 * s + 1] * dec;
+            };
+            // Q fragments (row tiles jt = 0..3) and K^T fragments (tiles 2s, 2s+1, token pairs 0, 1) of key
+            // group s; the base addresses are opaque so that the per-read constants stay in the instruction
+            // offsets instead of being hoisted as one address per read
+            auto bases = [&](int c, int (&qb)[4], int (&kb)[4]) {
 #pragma unroll
-                            for (int r2 = 0; r2 < 4; ++r2) {
-                                const int i = 16 * it + 4 * lg + r2;
-                                fvd[4 * it + r2] = (i < lc) ? lam_pow(l2, lc - 1 - i) : 0.f;
-                            }
+                for (int s = 0; s < 4; ++s) {
+                    qb[s] = kOffQ + (c % 3) * kQKTileB + q_off[s];
+                    kb[s] = kOffK + (c % 3) * kQKTileB + tr_off[s];
+                    asm("" : "+v"(qb[s]), "+v"(kb[s]));
+                }
+            };
+            auto load_qk = [&](const int (&qb)[4], const int (&kb)[4], int s, u32x4 (&qf)[4], u32x4 (&kf)[4]) {
+                if (kOut) {
+#pragma unroll
+                    for (int jt = 0; jt < 4; ++jt) qf[jt] = ld16(smem + qb[s] + 4096 * jt);
+                }
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int ip = 0; ip < 2; ++ip) {
+                        const uint8_t *src = smem + kb[s] + 8 * kk + (32 * ip) * 256;
+                        const u32x2 lo = ld_tr(src);
+                        const u32x2 hi = ld_tr(src + 16 * 256);
+                        kf[2 * kk + ip] = u32x4{lo.x, lo.y, hi.x, hi.y};
                     }
-                    const float dec = (lc == kC) ? dec64 : lam_pow(l2, lc);
-
-                    // the state before this chunk as bf16 hi + lo for the history term Q S^T; key group s holds
-                    // keys 32s + 8lg .. +7 in tiles 2s (slots 0..3) and 2s+1 (slots 4..7)
-                    u32x4 shi[4], slo[4];
-                    if (kOut) {
+            };
+            // key group s: history term acc += S_s Q^T (hi + lo) and state update S <- S + K^T V_dec (hi + lo)
+            auto group_mfma = [&](int s, const u32x4 &shi, const u32x4 &slo, const u32x4 (&qf)[4],
+                                  const u32x4 (&kf)[4], const u32x4 (&vdh)[2], const u32x4 (&vdl)[2]) {
+                if (kOut) {
 #pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            const u32x2 a = split_bf16x2(S[2 * s][0], S[2 * s][1]);
-                            const u32x2 b2 = split_bf16x2(S[2 * s][2], S[2 * s][3]);
-                            const u32x2 c2 = split_bf16x2(S[2 * s + 1][0], S[2 * s + 1][1]);
-                            const u32x2 d2 = split_bf16x2(S[2 * s + 1][2], S[2 * s + 1][3]);
-                            shi[s] = u32x4{a.x, b2.x, c2.x, d2.x};
-                            slo[s] = u32x4{a.y, b2.y, c2.y, d2.y};
-                        }
+                    for (int jt = 0; jt < 4; ++jt) {
+                        acc[jt] = mfma32(shi, qf[jt], acc[jt]);
+                        acc[jt] = mfma32(slo, qf[jt], acc[jt]);
                     }
+                }
 #pragma unroll
-                    for (int kt = 0; kt < 8; ++kt) S[kt] = S[kt] * dec;
-
-                    // V^T fragments of this wave's value tile, and V_dec = lambda^{lc-1-i} v_i as hi + lo
-                    u32x4 vf[2], vdh[2], vdl[2];
+                for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                    for (int it = 0; it < 4; ++it) {
-                        const u32x2 a = *reinterpret_cast<const u32x2 *>(tv + v_off + 2048 * it);
-                        const f32x4 x = mfma16(a, ident, f32x4{0.f, 0.f, 0.f, 0.f});
-                        const uint32_t x0 = pack_bf16x2(x[0], x[1]), x1 = pack_bf16x2(x[2], x[3]);
-                        const u32x2 d01 = split_bf16x2(x[0] * fvd[4 * it + 0], x[1] * fvd[4 * it + 1]);
-                        const u32x2 d23 = split_bf16x2(x[2] * fvd[4 * it + 2], x[3] * fvd[4 * it + 3]);
-                        if ((it & 1) == 0) {
-                            vf[it >> 1].x = x0; vf[it >> 1].y = x1;
-                            vdh[it >> 1].x = d01.x; vdh[it >> 1].y = d23.x;
-                            vdl[it >> 1].x = d01.y; vdl[it >> 1].y = d23.y;
-                        } else {
-                            vf[it >> 1].z = x0; vf[it >> 1].w = x1;
-                            vdh[it >> 1].z = d01.x; vdh[it >> 1].w = d23.x;
-                            vdl[it >> 1].z = d01.y; vdl[it >> 1].w = d23.y;
-                        }
+                    for (int ip = 0; ip < 2; ++ip) {
+                        S[2 * s + kk] = mfma32(kf[2 * kk + ip], vdh[ip], S[2 * s + kk]);
+                        S[2 * s + kk] = mfma32(kf[2 * kk + ip], vdl[ip], S[2 * s + kk]);
                     }
-
-                    // history term (acc) and state update S <- lambda^{lc} S + K^T V_dec, interleaved per key
-                    // group
-                    f32x4 acc[4];
+            };
+            auto load_p = [&](int c, u32x4 (&pf)[12]) {
+                const uint8_t *pbuf = smem + kOffP + (c & 1) * kPBufB + lane * 16;
 #pragma unroll
-                    for (int jt = 0; jt < 4; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int x = 0; x < 12; ++x) pf[x] = ld16(pbuf + x * kFragB);
+            };
+            // chunk c's output: O = scale lambda^{j+1} history + P.V (P carries scale), rounded to bf16 into the
+            // LDS output tile (row j, columns 16cw + 4lg .. +3 of the value half). Clears acc for the next chunk.
+            const int o_off = v_seg_off(lr, 2 * cw + (lg >> 1)) + 8 * (lg & 1);
+            auto output = [&](int c, const u32x4 (&pf)[12]) {
+                uint8_t *ot = smem + kOffO + (c & 1) * kOTileB + o_off;
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        if (kOut) {
+                for (int jt = 0; jt < 4; ++jt) {
+                    f32x4 a = acc[jt] * finter[jt];
 #pragma unroll
-                            for (int jt = 0; jt < 4; ++jt) {
-                                const u32x4 qf = ld16(tq + q_off[s] + 4096 * jt);
-                                acc[jt] = mfma32(shi[s], qf, acc[jt]);
-                                acc[jt] = mfma32(slo[s], qf, acc[jt]);
-                            }
-                        }
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk) {
-                            const int kt = 2 * s + kk;
-#pragma unroll
-                            for (int ip = 0; ip < 2; ++ip) {
-                                const u32x4 kf = ld16(ktbuf + (kt * 2 + ip) * kFragB);
-                                S[kt] = mfma32(kf, vdh[ip], S[kt]);
-                                S[kt] = mfma32(kf, vdl[ip], S[kt]);
-                            }
-                        }
+                    for (int ip = 0; ip <= (jt >> 1); ++ip) {
+                        a = mfma32(vf[ip], pf[2 * p_blk(jt, ip)], a);
+                        a = mfma32(vf[ip], pf[2 * p_blk(jt, ip) + 1], a);
                     }
+                    // row 16jt + lr: the swizzle term (row / 2) % 8 is the same for rows lr and 16jt + lr
+                    *reinterpret_cast<u32x2 *>(ot + 2048 * jt) = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+                    acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            };
 
-                    if (kOut) {
-                        // O = scale lambda^{j+1} history + P.V (P carries scale); rows j >= lc fall outside the
-                        // buffer range of the store and are dropped
-                        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-                            (void *)(p.o + ((row0 + c0) * p.HV + un.hv) * kDV + v0 + 16 * cw), 0,
-                            (lc - 1) * p.HV * kDV * 2 + 32, kBufDword3);
+            // One iteration: [output of chunk c-1] + V fragments, history term and state update of chunk c.
+            // LDS reads are issued one stage ahead of their use; scheduling fences keep the stages in order.
+            //   kind: bit 0 = chunk c-1 has an output, bit 1 = chunk c is the short last chunk
+            auto iteration = [&](int c, auto kind_tag) {
+                constexpr int kind = decltype(kind_tag)::value;
+                constexpr bool has_out = kOut && (kind & 1);
+                constexpr bool tail = (kind & 2) != 0;
+                float fvd[16];
+                float dec = dec64;
+                if (tail) {
+                    const int lc = min(kC, len - c * kC);
+                    tail_factors(lc, fvd);
+                    dec = lam_pow(l2, lc);
+                } else {
 #pragma unroll
-                        for (int jt = 0; jt < 4; ++jt) {
-                            f32x4 a = acc[jt] * finter[jt];
+                    for (int x = 0; x < 16; ++x) fvd[x] = fvd64[x];
+                }
+                int qb[4], kb[4];
+                bases(c, qb, kb);
+                u32x4 pf[12], qf[4], kf[4];
+                u32x2 va[4];
+                if (has_out) load_p(c - 1, pf);
+                load_v(c, va);
+                load_qk(qb, kb, 0, qf, kf);
+                __builtin_amdgcn_sched_barrier(0);
+                u32x4 shi, slo;
+                split_dec(0, dec, shi, slo);
+                if (has_out) output(c - 1, pf);
+                __builtin_amdgcn_sched_barrier(0);
+                u32x4 vdh[2], vdl[2];
 #pragma unroll
-                            for (int ip = 0; ip <= (jt >> 1); ++ip) {
-                                const uint8_t *blk = pbuf + p_blk(jt, ip) * 2 * kFragB + lane * 16;
-                                a = mfma32(vf[ip], *reinterpret_cast<const u32x4 *>(blk), a);
-                                a = mfma32(vf[ip], *reinterpret_cast<const u32x4 *>(blk + kFragB), a);
-                            }
-                            const int j = 16 * jt + lr;
-                            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])},
-                                                                  ro, j * (p.HV * kDV * 2) + 8 * lg, 0, 0);
-                        }
+                for (int s = 0; s < 4; ++s) {
+                    u32x4 qf2[4], kf2[4];
+                    if (s < 3) load_qk(qb, kb, s + 1, qf2, kf2);
+                    if (s == 0) {
+#pragma unroll
+                        for (int it = 0; it < 4; ++it) prep_part(va[it], it, fvd, vdh, vdl);
                     }
+                    group_mfma(s, shi, slo, qf, kf, vdh, vdl);
+                    if (s < 3) {
+                        split_dec(s + 1, dec, shi, slo);
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) { qf[x] = qf2[x]; kf[x] = kf2[x]; }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            using K_first_last = std::integral_constant<int, 2>;
+            using K_first = std::integral_constant<int, 0>;
+            using K_steady = std::integral_constant<int, 1>;
+            using K_last = std::integral_constant<int, 3>;
+
+            __syncthreads();
+            if (nch == 0) {
+                __syncthreads();
+            } else {
+                if (nch == 1)
+                    iteration(0, K_first_last{});
+                else
+                    iteration(0, K_first{});
+                __syncthreads();
+                // steady state: full chunks, no branches in the body
+                for (int c = 1; c < nch - 1; ++c) {
+                    iteration(c, K_steady{});
+                    __syncthreads();
+                }
+                if (nch >= 2) {
+                    iteration(nch - 1, K_last{});
+                    __syncthreads();
+                }
+                if (kOut) {
+                    u32x4 pf[12];
+                    load_p(nch - 1, pf);
+                    output(nch - 1, pf);
                 }
                 __syncthreads();
             }
@@ -505,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                 const int c0 = c * kC;
                 const int lc = min(kC, len - c0);
                 uint8_t *tq = smem + kOffQ + (c % 3) * kQKTileB;
-                uint8_t *tk = smem + kOffK + (c & 1) * kQKTileB;
+                uint8_t *tk = smem + kOffK + (c % 3) * kQKTileB;
                 uint8_t *tv = smem + kOffV + (c % 3) * kVTileB;
                 // buffer ranges end with the last valid row of the chunk; rows beyond read as zeros
                 const int qk_bytes = (lc - 1) * qk_stride + kD * 2;
@@ -537,15 +643,42 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                 default: score_factors<0, 2, 0, 2>(pf, l2, p.scale, lr, lg); break;
                 }
             }
+            // chunk c's output tile from LDS to HBM: producer wave cw stores rows 16cw .. 16cw+15 of the value
+            // half, 8 lanes of 16 B per 128-byte row half; rows >= lc fall outside the buffer range and are dropped
+            auto store_out = [&](int c) {
+                const int c0 = c * kC;
+                const int lc = min(kC, len - c0);
+                const uint8_t *ot = smem + kOffO + (c & 1) * kOTileB;
+                const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(p.o + ((row0 + c0) * p.HV + un.hv) * kDV + v0), 0, (lc - 1) * v_stride + kVW * 2,
+                    kBufDword3);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int r = 16 * cw + 8 * i + (lane >> 3);
+                    const u32x4 x = ld16(ot + v_seg_off(r, lane & 7));
+                    __builtin_amdgcn_raw_buffer_store_b128(x, ro, r * v_stride + 16 * (lane & 7), 0, 0);
+                }
+            };
+
+            // Loads complete in issue order: waiting until at most one chunk's loads are outstanding means the
+            // older chunk has landed in LDS. Output stores are issued after the loads of their iteration, so
+            // they can only make such a wait stricter.
             if (nch > 0) stage(0);
-            __builtin_amdgcn_s_waitcnt(0);
+            if (nch > 1) {
+                stage(1);
+                wait_vmcnt_lgkm0<kStageLoads>();
+            } else {
+                wait_vmcnt_lgkm0<0>();
+            }
             __syncthreads();
 
             for (int t = 0; t <= nch; ++t) {
-                if (t + 1 < nch) stage(t + 1);
+                const bool ahead = t + 2 < nch;
+                if (ahead) stage(t + 2);
+                if (kOut && t >= 2) store_out(t - 2);   // completed by the consumers before the last barrier
                 if (kOut && t < nch) {
                     const uint8_t *tq = smem + kOffQ + (t % 3) * kQKTileB;
-                    const uint8_t *tk = smem + kOffK + (t & 1) * kQKTileB;
+                    const uint8_t *tk = smem + kOffK + (t % 3) * kQKTileB;
                     uint8_t *pbuf = smem + kOffP + (t & 1) * kPBufB;
                     switch (cw) {
                     case 0: produce_scores<0, 2, 2, 1>(pf, tq, tk, pbuf, lane, lr, lg); break;
@@ -554,13 +687,16 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                     default: produce_scores<0, 2, 0, 2>(pf, tq, tk, pbuf, lane, lr, lg); break;
                     }
                 }
-                __builtin_amdgcn_s_waitcnt(0);      // staged rows of chunk t+1 have landed in LDS
+                if (ahead)
+                    wait_vmcnt_lgkm0<kStageLoads>();     // chunk t+1 has landed; chunk t+2 may be in flight
+                else
+                    wait_vmcnt_lgkm0<0>();
                 __syncthreads();
             }
+            if (kOut && nch > 0) store_out(nch - 1);
         }
     }
 }
-
 // ---------------------------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------------------------
