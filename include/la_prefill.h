@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 1
+#define LA_ABI_VERSION 2
 
 typedef enum {
     LA_OK = 0,
@@ -67,7 +67,9 @@ enum { LA_SCHED_AUTO = 0, LA_SCHED_PERSISTENT = 1, LA_SCHED_NONPERSISTENT = 2 };
  *   scale       : multiplies both the history term and the within-sequence term
  *   state_idx   : int32 [B] (device)
  * B == 0 or T == 0 is a no-op except that, with T == 0 and LA_STATE_WRITE, each selected slot receives its
- * initial state (S0 with LA_STATE_READ, else zeros).
+ * initial state (S0 with LA_STATE_READ, else zeros). Calls with 1 <= T <= 16 (draft-token verify and
+ * multi-token decode) take a one-pass kernel that evaluates the closed form from the initial state; longer
+ * ones take the 64-token chunked kernel.
  */
 la_status la_prefill_fwd(const void *q, const void *k, const void *v, void *o, int32_t B, int32_t T, int32_t H,
                          int32_t HV, int32_t D, int32_t DV, float scale, const float *slope, float *state_pool,
@@ -102,6 +104,42 @@ la_status la_prefill_fwd_varlen(const void *q, const void *k, const void *v, voi
 la_status la_state_commit(const void *k, const void *v, int32_t B, int32_t T, int32_t H, int32_t HV, int32_t D,
                           int32_t DV, const float *slope, float *state_pool, int32_t pool_size,
                           const int32_t *state_idx, const int32_t *accepted_len, hipStream_t stream);
+
+/*
+ * Fused multi-token decode (verify page, Description: fused MTP decode advances the recurrence over all T draft
+ * tokens per request and head in one launch): the outputs of all T tokens, and the state after them stored
+ * back into each request's slot, i.e. la_prefill_fwd with flags = LA_STATE_READ | LA_STATE_WRITE.
+ *   q, k        : bf16 [B, T, H, 128];  v, o : bf16 [B, T, HV, 128];  state_idx : int32 [B] (device)
+ *   state_pool, state_idx must be non-NULL. 1 <= T <= 16 runs in one pass; longer T are chunked.
+ */
+la_status la_decode_mtp(const void *q, const void *k, const void *v, void *o, int32_t B, int32_t T, int32_t H,
+                        int32_t HV, int32_t D, int32_t DV, float scale, const float *slope, float *state_pool,
+                        int32_t pool_size, const int32_t *state_idx, hipStream_t stream);
+
+/*
+ * Parallel verify with a KV buffer (verify page, Description: verify computes every draft step's output in
+ * closed form from the initial state without materialising intermediate states, and optionally writes k/v into
+ * a compact pooled KV buffer). Outputs as la_prefill_fwd with flags = LA_STATE_READ (the pool is only read).
+ * For every request b whose slot s = state_idx[b] is valid, the T draft rows of k and v are also copied to
+ *   k_buf : bf16 [pool_size, T, H, 128]   rows k_buf[s, t]      v_buf : bf16 [pool_size, T, HV, 128]
+ * so that la_state_commit_kvbuffer can advance the state later without the caller keeping k and v. Buffer
+ * slots of skipped requests (slot < 0 or >= pool_size) are not touched. k_buf and v_buf are both NULL (no
+ * buffer write) or both non-NULL. T <= 16, else LA_ERR_UNSUPPORTED.
+ */
+la_status la_verify_kvbuffer(const void *q, const void *k, const void *v, void *o, int32_t B, int32_t T, int32_t H,
+                             int32_t HV, int32_t D, int32_t DV, float scale, const float *slope,
+                             const float *state_pool, int32_t pool_size, const int32_t *state_idx, void *k_buf,
+                             void *v_buf, hipStream_t stream);
+
+/*
+ * Commit from the KV buffer (verify page, Description: state-update advances the pooled state by the per-request
+ * accepted prefix length L read from the buffer; padded slots are skipped; Tests: L = 0 is a no-op): as
+ * la_state_commit, with request b's token rows taken from k_buf[state_idx[b], 0 .. L-1] and
+ * v_buf[state_idx[b], 0 .. L-1] (layouts as written by la_verify_kvbuffer with the same T). T <= 16.
+ */
+la_status la_state_commit_kvbuffer(const void *k_buf, const void *v_buf, int32_t B, int32_t T, int32_t H, int32_t HV,
+                                   int32_t D, int32_t DV, const float *slope, float *state_pool, int32_t pool_size,
+                                   const int32_t *state_idx, const int32_t *accepted_len, hipStream_t stream);
 
 /* Static name of a status code. */
 const char *la_status_string(la_status s);

@@ -1,4 +1,4 @@
-"""Lightning Attention chunked prefill on AMD Instinct MI355X (gfx950).
+"""Lightning Attention prefill, multi-token decode and speculative verify / commit on AMD Instinct MI355X (gfx950).
 
 The computation lives in liblaprefill.so (C ABI: include/la_prefill.h); this package is its Python binding.
 Importing it fails loudly when the library has not been built.
@@ -15,8 +15,11 @@ from ._binding import (  # noqa: F401
     LA_STATE_READ,
     LA_STATE_WRITE,
     LaError,
+    la_decode_mtp,
     la_prefill_fwd,
     la_prefill_fwd_varlen,
     la_state_commit,
+    la_state_commit_kvbuffer,
+    la_verify_kvbuffer,
     lib,
 )

@@ -15,8 +15,8 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
 LA_STATE_READ, LA_STATE_WRITE = 1, 2
 LA_SCHED_AUTO, LA_SCHED_PERSISTENT, LA_SCHED_NONPERSISTENT = 0, 1, 2
 
-EXPORTS = ("la_prefill_fwd", "la_prefill_fwd_varlen", "la_state_commit", "la_status_string", "la_last_error",
-           "la_abi_version")
+EXPORTS = ("la_prefill_fwd", "la_prefill_fwd_varlen", "la_state_commit", "la_decode_mtp", "la_verify_kvbuffer",
+           "la_state_commit_kvbuffer", "la_status_string", "la_last_error", "la_abi_version")
 
 
 class LaError(RuntimeError):
@@ -40,6 +40,12 @@ def _load():
     L.la_prefill_fwd_varlen.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, u32, i32, p]
     L.la_state_commit.restype = ctypes.c_int
     L.la_state_commit.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p, p, i32, p, p, p]
+    L.la_decode_mtp.restype = ctypes.c_int
+    L.la_decode_mtp.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, p]
+    L.la_verify_kvbuffer.restype = ctypes.c_int
+    L.la_verify_kvbuffer.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, p, p, p]
+    L.la_state_commit_kvbuffer.restype = ctypes.c_int
+    L.la_state_commit_kvbuffer.argtypes = [p, p, i32, i32, i32, i32, i32, i32, p, p, i32, p, p, p]
     L.la_status_string.restype = ctypes.c_char_p
     L.la_status_string.argtypes = [ctypes.c_int]
     L.la_last_error.restype = ctypes.c_char_p
@@ -136,4 +142,70 @@ def la_state_commit(k, v, slope, state_pool, state_idx, accepted_len, stream=Non
     HV, DV = v.shape[2], v.shape[3]
     _check(lib.la_state_commit(_ptr(k), _ptr(v), B, T, H, HV, D, DV, _ptr(slope), _ptr(state_pool),
                                state_pool.shape[0], _ptr(state_idx), _ptr(accepted_len), _stream(stream, dev)))
+    return state_pool
+
+
+def _qkvo(q, k, v, o, dev):
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _req(t, n, torch.bfloat16, dev)
+    B, T, H, D = q.shape
+    HV, DV = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T) or o.shape != v.shape:
+        raise ValueError("shape mismatch between q, k, v, o")
+    return B, T, H, HV, D, DV
+
+
+def la_decode_mtp(q, k, v, o, slope, state_pool, state_idx, scale=1.0, stream=None):
+    """Multi-token decode: outputs of all T draft tokens, and each request's state advanced over them in place."""
+    import torch
+    dev = q.device
+    B, T, H, HV, D, DV = _qkvo(q, k, v, o, dev)
+    _req(slope, "slope", torch.float32, dev)
+    _req(state_pool, "state_pool", torch.float32, dev)
+    _req(state_idx, "state_idx", torch.int32, dev)
+    _check(lib.la_decode_mtp(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, HV, D, DV, float(scale), _ptr(slope),
+                             _ptr(state_pool), state_pool.shape[0], _ptr(state_idx), _stream(stream, dev)))
+    return o
+
+
+def la_verify_kvbuffer(q, k, v, o, slope, state_pool, state_idx, k_buf=None, v_buf=None, scale=1.0, stream=None):
+    """Verify T draft tokens from each request's pooled state (read only); optionally copy their k/v rows into
+    k_buf: bf16 [P, T, H, 128] and v_buf: bf16 [P, T, HV, 128] at the request's slot."""
+    import torch
+    dev = q.device
+    B, T, H, HV, D, DV = _qkvo(q, k, v, o, dev)
+    _req(slope, "slope", torch.float32, dev)
+    _req(state_pool, "state_pool", torch.float32, dev)
+    _req(state_idx, "state_idx", torch.int32, dev)
+    P = state_pool.shape[0]
+    for t, n, heads in ((k_buf, "k_buf", H), (v_buf, "v_buf", HV)):
+        _req(t, n, torch.bfloat16, dev)
+        if t is not None and tuple(t.shape) != (P, T, heads, 128):
+            raise ValueError(f"{n} must have shape {(P, T, heads, 128)}, got {tuple(t.shape)}")
+    _check(lib.la_verify_kvbuffer(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, HV, D, DV, float(scale), _ptr(slope),
+                                  _ptr(state_pool), P, _ptr(state_idx), _ptr(k_buf), _ptr(v_buf),
+                                  _stream(stream, dev)))
+    return o
+
+
+def la_state_commit_kvbuffer(k_buf, v_buf, slope, state_pool, state_idx, accepted_len, stream=None):
+    """Commit accepted draft tokens read from the KV buffer: k_buf: bf16 [P, T, H, 128]; v_buf: bf16
+    [P, T, HV, 128]; accepted_len: int32 [B]."""
+    import torch
+    dev = k_buf.device
+    _req(k_buf, "k_buf", torch.bfloat16, dev)
+    _req(v_buf, "v_buf", torch.bfloat16, dev)
+    _req(slope, "slope", torch.float32, dev)
+    _req(state_pool, "state_pool", torch.float32, dev)
+    _req(state_idx, "state_idx", torch.int32, dev)
+    _req(accepted_len, "accepted_len", torch.int32, dev)
+    P, T, H, D = k_buf.shape
+    HV, DV = v_buf.shape[2], v_buf.shape[3]
+    if v_buf.shape[:2] != (P, T) or state_pool.shape[0] != P:
+        raise ValueError("k_buf, v_buf and state_pool must share the slot count and T")
+    B = state_idx.shape[0]
+    _check(lib.la_state_commit_kvbuffer(_ptr(k_buf), _ptr(v_buf), B, T, H, HV, D, DV, _ptr(slope),
+                                        _ptr(state_pool), P, _ptr(state_idx), _ptr(accepted_len),
+                                        _stream(stream, dev)))
     return state_pool

@@ -37,24 +37,16 @@
 #include <stdarg.h>
 #include <string.h>
 
-#include "la_prefill.h"
+#include "la_common.h"
+
+using namespace la_detail;
 
 namespace {
 
 constexpr int kC = 64;                    // chunk length (tokens)
-constexpr int kD = 128;                   // key dim
-constexpr int kDV = 128;                  // value dim
 constexpr int kVSplit = 2;                // workgroups per (sequence, value head)
 constexpr int kVW = kDV / kVSplit;        // value columns per workgroup
 constexpr int kThreads = 512;             // 4 consumer waves (one 16-column value tile each) + 4 producer waves
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 enum Mode { kFixed = 0, kVarlen = 1, kCommit = 2 };
 
@@ -80,41 +72,6 @@ struct Params {
     float scale;
     uint32_t flags;
 };
-
-// ---------------------------------------------------------------------------------------------------------
-// small helpers
-// ---------------------------------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    f32x2 f = {a, b};
-    bf16x2 h = __builtin_convertvector(f, bf16x2);   // v_cvt_pk_bf16_f32, round to nearest even
-    return __builtin_bit_cast(uint32_t, h);
-}
-
-// x = hi + lo with hi = bf16(x), lo = bf16(x - hi); two values per call, returned as {hi pair, lo pair}.
-// The residual x - hi is exact in FP32; it is formed by one bf16 dot product against (-1, 0) or (0, -1)
-// accumulated onto x. The two masks are passed in registers: given the pair (-1, 0) as a constant, the
-// compiler encodes it as the inline constant -1.0, which the hardware reads as the FP32 bit pattern
-// 0xBF800000, i.e. the pair (0, -1).
-__device__ __forceinline__ u32x2 split_bf16x2(float a, float b) {
-    f32x2 f = {a, b};
-    const bf16x2 hi = __builtin_convertvector(f, bf16x2);
-    uint32_t m0 = 0x0000BF80u, m1 = 0xBF800000u;     // bf16 pairs (-1, 0) and (0, -1), element 0 low
-    asm("" : "+v"(m0), "+v"(m1));
-    const float ra = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, m0), a, false);
-    const float rb = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, m1), b, false);
-    return u32x2{__builtin_bit_cast(uint32_t, hi), pack_bf16x2(ra, rb)};
-}
-
-__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                   c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(u32x2 a, s16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), b, c, 0, 0, 0);
-}
-
-// lambda^n for n >= 0 given l2 = log2(lambda) (finite, <= 0).
-__device__ __forceinline__ float lam_pow(float l2, int n) { return __builtin_amdgcn_exp2f(l2 * (float)n); }
 
 struct Unit {
     int32_t seq, hv, vpart;
@@ -172,8 +129,6 @@ constexpr int kOTileB = kC * kVW * 2;        // 8192
 constexpr int kOffO = kOffP + 2 * kPBufB;
 constexpr int kLdsBytes = kOffO + 2 * kOTileB;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-
-constexpr int kBufDword3 = 0x00020000;       // buffer resource word 3: raw 32-bit data format
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -329,8 +284,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
         }
         if (MODE == kCommit && (slot < 0 || len == 0)) continue;   // skipped request / L = 0: no write at all
 
-        float l2 = -p.slope[un.hv] * 1.4426950408889634f;
-        l2 = fmaxf(l2, -1.0e30f);                                    // slope = +inf -> lambda^0 = 1, lambda^n = 0
+        const float l2 = log2_lambda(p.slope[un.hv]);
         const int nch = (len + kC - 1) / kC;
         const int qk_stride = p.H * kD * 2;                          // bytes between token rows
         const int v_stride = p.HV * kDV * 2;
@@ -697,10 +651,16 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
         }
     }
 }
+}  // namespace
+
 // ---------------------------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------------------------
+namespace la_detail {
+
 thread_local char g_err[512] = "";
+
+void clear_error() { g_err[0] = 0; }
 
 la_status fail(la_status s, const char *fmt, ...) {
     va_list ap;
@@ -727,6 +687,10 @@ la_status check_common(int32_t H, int32_t HV, int32_t D, int32_t DV, uint32_t fl
     return LA_OK;
 }
 
+}  // namespace la_detail
+
+namespace {
+
 template <int MODE>
 la_status launch(const Params &p, int grid, hipStream_t stream) {
     hipLaunchKernelGGL(la_chunk_kernel<MODE>, dim3(grid), dim3(kThreads), 0, stream, p);
@@ -742,7 +706,7 @@ extern "C" {
 la_status la_prefill_fwd(const void *q, const void *k, const void *v, void *o, int32_t B, int32_t T, int32_t H,
                          int32_t HV, int32_t D, int32_t DV, float scale, const float *slope, float *state_pool,
                          int32_t pool_size, const int32_t *state_idx, uint32_t flags, hipStream_t stream) {
-    g_err[0] = 0;
+    clear_error();
     la_status s = check_common(H, HV, D, DV, flags, slope, state_pool, pool_size, state_idx);
     if (s != LA_OK) return s;
     if (B < 0 || T < 0) return fail(LA_ERR_INVALID_ARG, "negative B or T (B=%d, T=%d)", B, T);
@@ -751,6 +715,13 @@ la_status la_prefill_fwd(const void *q, const void *k, const void *v, void *o, i
     if (T > 0 && (!q || !k || !v || !o)) return fail(LA_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
     if ((int64_t)B * HV * kVSplit > INT32_MAX) return fail(LA_ERR_UNSUPPORTED, "too many (sequence, head) units");
     if ((int64_t)B * T > INT32_MAX) return fail(LA_ERR_UNSUPPORTED, "B * T exceeds 2^31 - 1 tokens");
+    if (T >= 1 && T <= kShortMax) {
+        // a few tokens per sequence (verify / multi-token decode): one pass from the initial state
+        ShortCall c{};
+        c.q = q; c.k = k; c.v = v; c.o = o; c.slope = slope; c.pool = state_pool; c.state_idx = state_idx;
+        c.B = B; c.T = T; c.H = H; c.HV = HV; c.pool_size = pool_size; c.scale = scale; c.flags = flags;
+        return launch_short(c, stream);
+    }
     Params p{};
     p.q = (const uint16_t *)q; p.k = (const uint16_t *)k; p.v = (const uint16_t *)v; p.o = (uint16_t *)o;
     p.slope = slope; p.pool = state_pool; p.state_idx = state_idx;
@@ -764,7 +735,7 @@ la_status la_prefill_fwd_varlen(const void *q, const void *k, const void *v, voi
                                 int32_t N, int32_t total_T, int32_t H, int32_t HV, int32_t D, int32_t DV,
                                 float scale, const float *slope, float *state_pool, int32_t pool_size,
                                 const int32_t *state_idx, uint32_t flags, int32_t schedule, hipStream_t stream) {
-    g_err[0] = 0;
+    clear_error();
     la_status s = check_common(H, HV, D, DV, flags, slope, state_pool, pool_size, state_idx);
     if (s != LA_OK) return s;
     if (N < 0 || total_T < 0) return fail(LA_ERR_INVALID_ARG, "negative N or total_T (N=%d, total_T=%d)", N, total_T);
@@ -796,7 +767,7 @@ la_status la_prefill_fwd_varlen(const void *q, const void *k, const void *v, voi
 la_status la_state_commit(const void *k, const void *v, int32_t B, int32_t T, int32_t H, int32_t HV, int32_t D,
                           int32_t DV, const float *slope, float *state_pool, int32_t pool_size,
                           const int32_t *state_idx, const int32_t *accepted_len, hipStream_t stream) {
-    g_err[0] = 0;
+    clear_error();
     la_status s = check_common(H, HV, D, DV, LA_STATE_READ | LA_STATE_WRITE, slope, state_pool, pool_size,
                                state_idx);
     if (s != LA_OK) return s;
@@ -805,6 +776,13 @@ la_status la_state_commit(const void *k, const void *v, int32_t B, int32_t T, in
     if (!k || !v || !accepted_len) return fail(LA_ERR_INVALID_ARG, "k, v and accepted_len must be non-NULL");
     if ((int64_t)B * HV * kVSplit > INT32_MAX) return fail(LA_ERR_UNSUPPORTED, "too many (request, head) units");
     if ((int64_t)B * T > INT32_MAX) return fail(LA_ERR_UNSUPPORTED, "B * T exceeds 2^31 - 1 tokens");
+    if (T <= kShortMax) {
+        ShortCall c{};
+        c.k = k; c.v = v; c.slope = slope; c.pool = state_pool; c.state_idx = state_idx;
+        c.accepted_len = accepted_len; c.B = B; c.T = T; c.H = H; c.HV = HV; c.pool_size = pool_size;
+        c.scale = 1.0f; c.flags = LA_STATE_READ | LA_STATE_WRITE; c.commit = true;
+        return launch_short(c, stream);
+    }
     Params p{};
     p.k = (const uint16_t *)k; p.v = (const uint16_t *)v;
     p.accepted_len = accepted_len; p.slope = slope; p.pool = state_pool; p.state_idx = state_idx;
@@ -824,7 +802,7 @@ const char *la_status_string(la_status s) {
     return "LA_ERR_UNKNOWN";
 }
 
-const char *la_last_error(void) { return g_err; }
+const char *la_last_error(void) { return la_detail::g_err; }
 
 int32_t la_abi_version(void) { return LA_ABI_VERSION; }
 

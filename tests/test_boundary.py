@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert L.la_abi_version() == 1
+    assert L.la_abi_version() == 2
     assert L.la_status_string(0) == b"LA_OK"
     assert L.la_status_string(2) == b"LA_ERR_UNSUPPORTED"
 
@@ -86,6 +86,28 @@ def test_commit_rejects_before_launch():
     assert f(FAKE, FAKE, 2, 8, 2, 2, 128, 128, FAKE, None, 4, FAKE, FAKE, None) == la.LA_ERR_INVALID_ARG
     assert f(FAKE, FAKE, 2, 8, 2, 2, 128, 128, FAKE, FAKE, 4, FAKE, None, None) == la.LA_ERR_INVALID_ARG
     assert f(FAKE, FAKE, 2, 8, 2, 3, 128, 128, FAKE, FAKE, 4, FAKE, FAKE, None) == la.LA_ERR_UNSUPPORTED
+
+
+def test_short_path_entry_points_reject_before_launch():
+    # decode: needs a pool and indices (it reads and writes the state)
+    assert L.la_decode_mtp(FAKE, FAKE, FAKE, FAKE, 2, 4, 2, 2, 128, 128, 1.0, FAKE, None, 4, FAKE, None) == \
+        la.LA_ERR_INVALID_ARG
+    assert L.la_decode_mtp(FAKE, FAKE, FAKE, FAKE, 2, 4, 2, 2, 64, 128, 1.0, FAKE, FAKE, 4, FAKE, None) == \
+        la.LA_ERR_UNSUPPORTED
+    v = L.la_verify_kvbuffer
+    assert v(FAKE, FAKE, FAKE, FAKE, 2, 17, 2, 2, 128, 128, 1.0, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == \
+        la.LA_ERR_UNSUPPORTED                                      # more than 16 draft tokens
+    assert v(FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 2, 128, 128, 1.0, FAKE, FAKE, 4, FAKE, FAKE, None, None) == \
+        la.LA_ERR_INVALID_ARG                                      # k_buf without v_buf
+    assert v(FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 2, 128, 128, 1.0, FAKE, None, 4, FAKE, None, None, None) == \
+        la.LA_ERR_INVALID_ARG                                      # verify reads the pool
+    assert v(FAKE, FAKE, FAKE, FAKE, 0, 8, 2, 2, 128, 128, 1.0, FAKE, FAKE, 4, FAKE, None, None, None) == la.LA_OK
+    c = L.la_state_commit_kvbuffer
+    assert c(FAKE, FAKE, 2, 17, 2, 2, 128, 128, FAKE, FAKE, 4, FAKE, FAKE, None) == la.LA_ERR_UNSUPPORTED
+    assert c(FAKE, None, 2, 8, 2, 2, 128, 128, FAKE, FAKE, 4, FAKE, FAKE, None) == la.LA_ERR_INVALID_ARG
+    assert c(FAKE, FAKE, 2, 8, 2, 2, 128, 128, FAKE, FAKE, 4, FAKE, None, None) == la.LA_ERR_INVALID_ARG
+    assert c(FAKE, FAKE, 2, 8, 3, 2, 128, 128, FAKE, FAKE, 4, FAKE, FAKE, None) == la.LA_ERR_UNSUPPORTED
+    assert c(FAKE, FAKE, 2, 0, 2, 2, 128, 128, FAKE, FAKE, 4, FAKE, FAKE, None) == la.LA_OK
 
 
 def test_python_binding_rejects_bad_tensors():
