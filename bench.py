@@ -3,7 +3,8 @@
 One step = one la_prefill_fwd call over the whole workload: B=2, T=8192, H=HV=64, D=DV=128, bf16 Q/K/V/O,
 FP32 state read from and written back to a 2-slot pool in place (every step sees the previous step's state;
 the work per step is identical). Inputs are synthetic (la_synth recipe, seed 1) and resident in HBM before the
-timed region. Prints one JSON line.
+timed region. Prints one JSON line. --config 0/2/3 time the other prefill workloads; --config 4 times the draft
+verify + commit chain through the KV buffer (B=128 requests, T=8).
 
   python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--config {0,1,2,3,4}]
 """
@@ -22,6 +23,21 @@ METRIC = "LA prefill Mtok·head/s and % MFMA/HBM roofline at B=2,T=8192,H=64,D=1
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2516.6    # MI355X dense bf16 matrix peak
 CHUNK = 64
+
+
+def chain_bytes(w):
+    """Verify + commit through the KV buffer (B requests, T drafts): verify reads q, k, v and each valid slot's
+    state, writes o and copies k, v into the buffer; commit reads the first L_b buffer rows and reads and writes
+    the state of every valid request with L_b > 0."""
+    P = w.pool.shape[0]
+    valid = [0 <= int(s) < P for s in w.state_idx]
+    nvalid = sum(valid)
+    tok = w.B * w.T
+    verify = tok * (2 * w.H + 2 * w.HV) * 256 + nvalid * w.T * (w.H + w.HV) * 256 + nvalid * w.HV * 65536
+    acc_rows = sum(int(l) for l, ok in zip(w.accepted_len, valid) if ok)
+    ncommit = sum(1 for l, ok in zip(w.accepted_len, valid) if ok and int(l) > 0)
+    commit = acc_rows * (w.H + w.HV) * 256 + ncommit * w.HV * 65536 * 2
+    return verify + commit
 
 
 def algorithmic_bytes(w):
@@ -53,22 +69,35 @@ def mfma_flops_executed(w):
     return per_chunk_head * chunks * w.HV
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "la_chunk_kernel_fixed_b2_t8192_h64_hbm_traffic.md")
-KERNEL_SRC = os.path.join(ROOT, "linear_attention_decay_amd", "csrc", "la_prefill.hip")
+CSRC = os.path.join(ROOT, "linear_attention_decay_amd", "csrc")
+TRAFFIC = {   # workload -> (committed FETCH_SIZE / WRITE_SIZE summary, kernel sources it was measured on)
+    1: (os.path.join(ROOT, "profiles", "la_chunk_kernel_fixed_b2_t8192_h64_hbm_traffic.md"),
+        ("la_common.h", "la_prefill.hip")),
+    4: (os.path.join(ROOT, "profiles", "la_short_kernel_verify_commit_b128_t8_h64_hbm_traffic.md"),
+        ("la_common.h", "la_short.hip")),
+}
+
+
+def kernel_source_sha(names):
+    """sha256 over the concatenated kernel sources (the key a traffic summary records)."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(CSRC, n), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(config):
-    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary, if it was taken on this kernel
-    source and this workload; else None."""
-    import hashlib
-    if config != 1 or not os.path.exists(TRAFFIC_FILE):
+    """HBM bytes per step from the committed FETCH_SIZE/WRITE_SIZE summary, if it was taken on these kernel
+    sources and this workload; else None."""
+    if config not in TRAFFIC or not os.path.exists(TRAFFIC[config][0]):
         return None
-    txt = open(TRAFFIC_FILE).read()
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if f"Kernel source sha256: {sha}" not in txt:
+    path, srcs = TRAFFIC[config]
+    txt = open(path).read()
+    if f"Kernel source sha256: {kernel_source_sha(srcs)}" not in txt:
         return None
     for line in txt.splitlines():
-        if line.startswith("traffic_bytes_per_launch:"):
+        if line.startswith("traffic_bytes_per_step:") or line.startswith("traffic_bytes_per_launch:"):
             return int(line.split(":")[1])
     return None
 
@@ -147,8 +176,17 @@ def main():
     flags = w.flags
     stream = torch.cuda.current_stream(dev)
 
+    chain = w.accepted_len is not None      # verify + commit of draft tokens through the KV buffer
+    if chain:
+        acc = to_dev(w.accepted_len)
+        kb = torch.empty((w.pool.shape[0], w.T, w.H, 128), dtype=torch.bfloat16, device=dev)
+        vb = torch.empty((w.pool.shape[0], w.T, w.HV, 128), dtype=torch.bfloat16, device=dev)
+
     def step():
-        if cu is None:
+        if chain:
+            la.la_verify_kvbuffer(q, k, v, o, slope, pool, idx, k_buf=kb, v_buf=vb, scale=w.scale, stream=stream)
+            la.la_state_commit_kvbuffer(kb, vb, slope, pool, idx, acc, stream=stream)
+        elif cu is None:
             la.la_prefill_fwd(q, k, v, o, slope, scale=w.scale, state_pool=pool, state_idx=idx, flags=flags,
                               stream=stream)
         else:
@@ -191,9 +229,10 @@ def main():
 
     tokheads = w.tokens * w.HV
     value = tokheads / (ms_per_step * 1e-3) / 1e6
-    alg_bytes = algorithmic_bytes(w)
+    alg_bytes = chain_bytes(w) if chain else algorithmic_bytes(w)
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    mfma_tfs = mfma_flops_executed(w) / (kern_ms * 1e-3) / 1e12
+    short = chain or 1 <= w.T <= 16
+    mfma_tfs = None if short else mfma_flops_executed(w) / (kern_ms * 1e-3) / 1e12
 
     out = {
         "metric": METRIC,
@@ -213,10 +252,13 @@ def main():
                    "chunk": CHUNK, "state_flags": w.flags, "tokens": w.tokens},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
-                     "kernel": "la_chunk_kernel<0>", "kernel_ms_avg": round(kern_ms, 6),
+                     "kernel": ("la_short_kernel<false> + la_short_kernel<true> (verify + commit)" if chain else
+                                "la_short_kernel<false>" if 1 <= w.T <= 16 else
+                                "la_chunk_kernel<1>" if cu is not None else "la_chunk_kernel<0>"),
+                     "kernel_ms_avg": round(kern_ms, 6),
                      "kernel_ms_median": round(per[len(per) // 2], 6), "algorithmic_bytes": alg_bytes},
-        "mfma": {"executed_tflops": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
-                 "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)},
+        "mfma": None if short else {"executed_tflops": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                                    "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)},
     }
     if not args.no_cpu_baseline and args.config in (0, 1):
         out["cpu_baseline"] = cpu_baseline(w)
