@@ -32,6 +32,7 @@
  *   - Host-checkable problems return an error before anything is enqueued:
  *       D != 128, DV != 128, H <= 0, HV % H != 0            -> LA_ERR_UNSUPPORTED
  *       negative sizes, NULL required pointer, bad flags     -> LA_ERR_INVALID_ARG
+ *     A NULL state_pool / state_idx is allowed when flags holds neither LA_STATE_READ nor LA_STATE_WRITE.
  *     A call with no tokens and no sequences is a successful no-op. A launch failure returns LA_ERR_HIP.
  *     la_last_error() then describes the failure (thread-local).
  */
@@ -54,8 +55,10 @@ typedef enum {
     LA_ERR_HIP = 3
 } la_status;
 
-/* flags bitmask */
-enum { LA_STATE_READ = 1u, LA_STATE_WRITE = 2u };
+/* flags bitmask. LA_DECAY_PER_QK_HEAD (prefill page, Performance: the GVA rows with decay owned per value head,
+ * "_hv", and per q/k head, "_h"): slope has H entries and value head hv uses slope[hv / (HV / H)]; without it
+ * slope has HV entries. */
+enum { LA_STATE_READ = 1u, LA_STATE_WRITE = 2u, LA_DECAY_PER_QK_HEAD = 4u };
 
 /* packed-sequence scheduling */
 enum { LA_SCHED_AUTO = 0, LA_SCHED_PERSISTENT = 1, LA_SCHED_NONPERSISTENT = 2 };
@@ -76,6 +79,19 @@ la_status la_prefill_fwd(const void *q, const void *k, const void *v, void *o, i
                          int32_t pool_size, const int32_t *state_idx, uint32_t flags, hipStream_t stream);
 
 /*
+ * As la_prefill_fwd, with the final state stored into a slot of its own (prefill page, comparison notes:
+ * indirect / shared state-pool ownership). Sequence b reads its initial state from state_idx[b] (LA_STATE_READ)
+ * and stores its final state into state_idx_out[b] (LA_STATE_WRITE); an out slot < 0 or >= pool_size stores
+ * nothing. Several sequences may read the same slot. A slot that one sequence writes must not be read or
+ * written by another sequence of the same call (undefined). state_idx_out == NULL means state_idx.
+ *   state_idx_out : int32 [B] (device)
+ */
+la_status la_prefill_fwd_ex(const void *q, const void *k, const void *v, void *o, int32_t B, int32_t T, int32_t H,
+                            int32_t HV, int32_t D, int32_t DV, float scale, const float *slope, float *state_pool,
+                            int32_t pool_size, const int32_t *state_idx, const int32_t *state_idx_out,
+                            uint32_t flags, hipStream_t stream);
+
+/*
  * Packed variable-length prefill (prefill page, Description: packed variable-length BF16 prefill; persistent
  * or non-persistent packed scheduling). Sequence n occupies token rows [cu_seqlens[n], cu_seqlens[n+1]);
  * chunks never straddle sequences.
@@ -90,6 +106,14 @@ la_status la_prefill_fwd_varlen(const void *q, const void *k, const void *v, voi
                                 int32_t N, int32_t total_T, int32_t H, int32_t HV, int32_t D, int32_t DV,
                                 float scale, const float *slope, float *state_pool, int32_t pool_size,
                                 const int32_t *state_idx, uint32_t flags, int32_t schedule, hipStream_t stream);
+
+/* As la_prefill_fwd_varlen, with a separate out slot per sequence (state_idx_out: int32 [N]; semantics as
+ * la_prefill_fwd_ex). */
+la_status la_prefill_fwd_varlen_ex(const void *q, const void *k, const void *v, void *o, const int32_t *cu_seqlens,
+                                   int32_t N, int32_t total_T, int32_t H, int32_t HV, int32_t D, int32_t DV,
+                                   float scale, const float *slope, float *state_pool, int32_t pool_size,
+                                   const int32_t *state_idx, const int32_t *state_idx_out, uint32_t flags,
+                                   int32_t schedule, hipStream_t stream);
 
 /*
  * Commit after a short-chunk verify (verify page, Description: state-update advances the pooled state by the

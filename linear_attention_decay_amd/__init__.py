@@ -5,6 +5,7 @@ Importing it fails loudly when the library has not been built.
 """
 from ._binding import (  # noqa: F401
     EXPORTS,
+    LA_DECAY_PER_QK_HEAD,
     LA_ERR_HIP,
     LA_ERR_INVALID_ARG,
     LA_ERR_UNSUPPORTED,
@@ -17,7 +18,9 @@ from ._binding import (  # noqa: F401
     LaError,
     la_decode_mtp,
     la_prefill_fwd,
+    la_prefill_fwd_ex,
     la_prefill_fwd_varlen,
+    la_prefill_fwd_varlen_ex,
     la_state_commit,
     la_state_commit_kvbuffer,
     la_verify_kvbuffer,

@@ -12,11 +12,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liblaprefill.so")
 
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
-LA_STATE_READ, LA_STATE_WRITE = 1, 2
+LA_STATE_READ, LA_STATE_WRITE, LA_DECAY_PER_QK_HEAD = 1, 2, 4
 LA_SCHED_AUTO, LA_SCHED_PERSISTENT, LA_SCHED_NONPERSISTENT = 0, 1, 2
 
-EXPORTS = ("la_prefill_fwd", "la_prefill_fwd_varlen", "la_state_commit", "la_decode_mtp", "la_verify_kvbuffer",
-           "la_state_commit_kvbuffer", "la_status_string", "la_last_error", "la_abi_version")
+EXPORTS = ("la_prefill_fwd", "la_prefill_fwd_ex", "la_prefill_fwd_varlen", "la_prefill_fwd_varlen_ex",
+           "la_state_commit", "la_decode_mtp", "la_verify_kvbuffer", "la_state_commit_kvbuffer", "la_status_string",
+           "la_last_error", "la_abi_version")
 
 
 class LaError(RuntimeError):
@@ -36,6 +37,11 @@ def _load():
     p, i32, u32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float
     L.la_prefill_fwd.restype = ctypes.c_int
     L.la_prefill_fwd.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, u32, p]
+    L.la_prefill_fwd_ex.restype = ctypes.c_int
+    L.la_prefill_fwd_ex.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, p, u32, p]
+    L.la_prefill_fwd_varlen_ex.restype = ctypes.c_int
+    L.la_prefill_fwd_varlen_ex.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, p, u32, i32,
+                                           p]
     L.la_prefill_fwd_varlen.restype = ctypes.c_int
     L.la_prefill_fwd_varlen.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, u32, i32, p]
     L.la_state_commit.restype = ctypes.c_int
@@ -85,9 +91,19 @@ def _req(t, name, dtype, dev):
         raise ValueError(f"{name} must be contiguous")
 
 
-def la_prefill_fwd(q, k, v, o, slope, scale=1.0, state_pool=None, state_idx=None, flags=0, stream=None):
-    """Fixed-length prefill. q, k: bf16 [B, T, H, 128]; v, o: bf16 [B, T, HV, 128]; slope: fp32 [HV];
-    state_pool: fp32 [P, HV, 128, 128]; state_idx: int32 [B]; flags: LA_STATE_READ | LA_STATE_WRITE."""
+def _slope_len(slope, flags, H, HV):
+    want = H if flags & LA_DECAY_PER_QK_HEAD else HV
+    if slope.numel() != want:
+        raise ValueError(f"slope must have {want} entries, got {slope.numel()}")
+
+
+def la_prefill_fwd(q, k, v, o, slope, scale=1.0, state_pool=None, state_idx=None, flags=0, stream=None,
+                   state_idx_out=None):
+    """Fixed-length prefill. q, k: bf16 [B, T, H, 128]; v, o: bf16 [B, T, HV, 128]; slope: fp32 [HV] (or [H] with
+    LA_DECAY_PER_QK_HEAD); state_pool: fp32 [P, HV, 128, 128]; state_idx: int32 [B]; flags: LA_STATE_READ |
+    LA_STATE_WRITE | LA_DECAY_PER_QK_HEAD. state_idx_out (int32 [B]) selects la_prefill_fwd_ex."""
+    if state_idx_out is not None:
+        return la_prefill_fwd_ex(q, k, v, o, slope, scale, state_pool, state_idx, state_idx_out, flags, stream)
     import torch
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
@@ -99,15 +115,35 @@ def la_prefill_fwd(q, k, v, o, slope, scale=1.0, state_pool=None, state_idx=None
     HV, DV = v.shape[2], v.shape[3]
     if k.shape != q.shape or v.shape[:2] != (B, T) or o.shape != v.shape:
         raise ValueError("shape mismatch between q, k, v, o")
+    _slope_len(slope, flags, H, HV)
     P = 0 if state_pool is None else state_pool.shape[0]
     _check(lib.la_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, HV, D, DV, float(scale), _ptr(slope),
                               _ptr(state_pool), P, _ptr(state_idx), int(flags), _stream(stream, dev)))
     return o
 
 
+def la_prefill_fwd_ex(q, k, v, o, slope, scale=1.0, state_pool=None, state_idx=None, state_idx_out=None, flags=0,
+                      stream=None):
+    """Fixed-length prefill whose final states go to state_idx_out (int32 [B]) instead of state_idx."""
+    import torch
+    dev = q.device
+    B, T, H, HV, D, DV = _qkvo(q, k, v, o, dev)
+    _req(slope, "slope", torch.float32, dev)
+    _req(state_pool, "state_pool", torch.float32, dev)
+    _req(state_idx, "state_idx", torch.int32, dev)
+    _req(state_idx_out, "state_idx_out", torch.int32, dev)
+    _slope_len(slope, flags, H, HV)
+    P = 0 if state_pool is None else state_pool.shape[0]
+    _check(lib.la_prefill_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, HV, D, DV, float(scale), _ptr(slope),
+                                 _ptr(state_pool), P, _ptr(state_idx), _ptr(state_idx_out), int(flags),
+                                 _stream(stream, dev)))
+    return o
+
+
 def la_prefill_fwd_varlen(q, k, v, o, cu_seqlens, slope, scale=1.0, state_pool=None, state_idx=None, flags=0,
-                          schedule=LA_SCHED_AUTO, stream=None):
-    """Packed prefill. q, k: bf16 [total_T, H, 128]; v, o: bf16 [total_T, HV, 128]; cu_seqlens: int32 [N+1]."""
+                          schedule=LA_SCHED_AUTO, stream=None, state_idx_out=None):
+    """Packed prefill. q, k: bf16 [total_T, H, 128]; v, o: bf16 [total_T, HV, 128]; cu_seqlens: int32 [N+1].
+    state_idx_out (int32 [N]) selects la_prefill_fwd_varlen_ex."""
     import torch
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
@@ -120,12 +156,26 @@ def la_prefill_fwd_varlen(q, k, v, o, cu_seqlens, slope, scale=1.0, state_pool=N
     HV, DV = v.shape[1], v.shape[2]
     if k.shape != q.shape or v.shape[0] != total_T or o.shape != v.shape:
         raise ValueError("shape mismatch between q, k, v, o")
+    _req(state_idx_out, "state_idx_out", torch.int32, dev)
+    _slope_len(slope, flags, H, HV)
     N = cu_seqlens.shape[0] - 1
     P = 0 if state_pool is None else state_pool.shape[0]
-    _check(lib.la_prefill_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens), N, total_T, H, HV, D, DV,
-                                     float(scale), _ptr(slope), _ptr(state_pool), P, _ptr(state_idx), int(flags),
-                                     int(schedule), _stream(stream, dev)))
+    if state_idx_out is None:
+        _check(lib.la_prefill_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens), N, total_T, H, HV, D,
+                                         DV, float(scale), _ptr(slope), _ptr(state_pool), P, _ptr(state_idx),
+                                         int(flags), int(schedule), _stream(stream, dev)))
+    else:
+        _check(lib.la_prefill_fwd_varlen_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens), N, total_T, H, HV,
+                                            D, DV, float(scale), _ptr(slope), _ptr(state_pool), P, _ptr(state_idx),
+                                            _ptr(state_idx_out), int(flags), int(schedule), _stream(stream, dev)))
     return o
+
+
+def la_prefill_fwd_varlen_ex(q, k, v, o, cu_seqlens, slope, scale=1.0, state_pool=None, state_idx=None,
+                             state_idx_out=None, flags=0, schedule=LA_SCHED_AUTO, stream=None):
+    """Packed prefill whose final states go to state_idx_out (int32 [N]) instead of state_idx."""
+    return la_prefill_fwd_varlen(q, k, v, o, cu_seqlens, slope, scale, state_pool, state_idx, flags, schedule, stream,
+                                 state_idx_out=state_idx_out)
 
 
 def la_state_commit(k, v, slope, state_pool, state_idx, accepted_len, stream=None):

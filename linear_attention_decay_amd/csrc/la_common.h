@@ -78,6 +78,7 @@ struct ShortCall {
     const float *slope;
     float *pool;
     const int32_t *state_idx, *accepted_len;
+    const int32_t *state_idx_out;  // slot that receives the final state; NULL: the slot read from
     int32_t B, T, H, HV, pool_size;
     float scale;
     uint32_t flags;

@@ -60,6 +60,7 @@ struct Params {
     const float *slope;
     float *pool;
     const int32_t *state_idx;
+    const int32_t *state_idx_out;   // slot that receives the final state; NULL: the slot read from
     int32_t nseq;
     int32_t T;          // fixed / commit: tokens per sequence
     int32_t total_T;    // varlen: rows in q/k/v
@@ -277,19 +278,25 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
             row0 = (int64_t)un.seq * p.T;
             len = p.T;
         }
-        int slot = -1;
-        if (p.flags != 0) {
+        int slot = -1, slot_out = -1;
+        if (p.flags & (LA_STATE_READ | LA_STATE_WRITE)) {
             const int s = p.state_idx[un.seq];
             if (s >= 0 && s < p.pool_size) slot = s;
+            slot_out = slot;
+            if (p.state_idx_out) {
+                const int so = p.state_idx_out[un.seq];
+                slot_out = (so >= 0 && so < p.pool_size) ? so : -1;
+            }
         }
         if (MODE == kCommit && (slot < 0 || len == 0)) continue;   // skipped request / L = 0: no write at all
 
-        const float l2 = log2_lambda(p.slope[un.hv]);
+        const float l2 = log2_lambda(p.slope[(p.flags & LA_DECAY_PER_QK_HEAD) ? h : un.hv]);
         const int nch = (len + kC - 1) / kC;
         const int qk_stride = p.H * kD * 2;                          // bytes between token rows
         const int v_stride = p.HV * kDV * 2;
-        float *plane = nullptr;
+        float *plane = nullptr, *plane_out = nullptr;
         if (slot >= 0) plane = p.pool + ((int64_t)slot * p.HV + un.hv) * (kDV * kD);
+        if (slot_out >= 0) plane_out = p.pool + ((int64_t)slot_out * p.HV + un.hv) * (kDV * kD);
 
         // The two roles run separate code with the same number of workgroup barriers (nch + 2 per unit), so
         // each role's loop-carried registers are allocated on their own.
@@ -535,10 +542,10 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                 __syncthreads();
             }
 
-            if (slot >= 0 && (p.flags & LA_STATE_WRITE)) {
+            if (slot_out >= 0 && (p.flags & LA_STATE_WRITE)) {
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt)
-                    *reinterpret_cast<f32x4 *>(plane + vrow * kD + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1)) = S[kt];
+                    *reinterpret_cast<f32x4 *>(plane_out + vrow * kD + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1)) = S[kt];
             }
         } else {
             // ======================================== producer: staging and scores / P
@@ -678,11 +685,11 @@ la_status check_common(int32_t H, int32_t HV, int32_t D, int32_t DV, uint32_t fl
         return fail(LA_ERR_UNSUPPORTED, "head counts must be positive (H=%d, HV=%d)", H, HV);
     if (HV % H != 0)
         return fail(LA_ERR_UNSUPPORTED, "HV (%d) must be a multiple of H (%d)", HV, H);
-    if (flags & ~(uint32_t)(LA_STATE_READ | LA_STATE_WRITE))
+    if (flags & ~(uint32_t)(LA_STATE_READ | LA_STATE_WRITE | LA_DECAY_PER_QK_HEAD))
         return fail(LA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
     if (!slope) return fail(LA_ERR_INVALID_ARG, "slope is NULL");
     if (pool_size < 0) return fail(LA_ERR_INVALID_ARG, "pool_size is negative");
-    if (flags && (!pool || !state_idx))
+    if ((flags & (LA_STATE_READ | LA_STATE_WRITE)) && (!pool || !state_idx))
         return fail(LA_ERR_INVALID_ARG, "state flags set but state_pool or state_idx is NULL");
     return LA_OK;
 }
@@ -703,9 +710,10 @@ la_status launch(const Params &p, int grid, hipStream_t stream) {
 
 extern "C" {
 
-la_status la_prefill_fwd(const void *q, const void *k, const void *v, void *o, int32_t B, int32_t T, int32_t H,
-                         int32_t HV, int32_t D, int32_t DV, float scale, const float *slope, float *state_pool,
-                         int32_t pool_size, const int32_t *state_idx, uint32_t flags, hipStream_t stream) {
+la_status la_prefill_fwd_ex(const void *q, const void *k, const void *v, void *o, int32_t B, int32_t T, int32_t H,
+                            int32_t HV, int32_t D, int32_t DV, float scale, const float *slope, float *state_pool,
+                            int32_t pool_size, const int32_t *state_idx, const int32_t *state_idx_out,
+                            uint32_t flags, hipStream_t stream) {
     clear_error();
     la_status s = check_common(H, HV, D, DV, flags, slope, state_pool, pool_size, state_idx);
     if (s != LA_OK) return s;
@@ -719,22 +727,31 @@ la_status la_prefill_fwd(const void *q, const void *k, const void *v, void *o, i
         // a few tokens per sequence (verify / multi-token decode): one pass from the initial state
         ShortCall c{};
         c.q = q; c.k = k; c.v = v; c.o = o; c.slope = slope; c.pool = state_pool; c.state_idx = state_idx;
+        c.state_idx_out = state_idx_out;
         c.B = B; c.T = T; c.H = H; c.HV = HV; c.pool_size = pool_size; c.scale = scale; c.flags = flags;
         return launch_short(c, stream);
     }
     Params p{};
     p.q = (const uint16_t *)q; p.k = (const uint16_t *)k; p.v = (const uint16_t *)v; p.o = (uint16_t *)o;
-    p.slope = slope; p.pool = state_pool; p.state_idx = state_idx;
+    p.slope = slope; p.pool = state_pool; p.state_idx = state_idx; p.state_idx_out = state_idx_out;
     p.nseq = B; p.T = T; p.total_T = B * T; p.H = H; p.HV = HV; p.G = HV / H;
-    p.pool_size = flags ? pool_size : 0; p.npairs = B * HV; p.nunits = p.npairs * kVSplit;
+    p.pool_size = (flags & (LA_STATE_READ | LA_STATE_WRITE)) ? pool_size : 0; p.npairs = B * HV; p.nunits = p.npairs * kVSplit;
     p.scale = scale; p.flags = flags;
     return launch<kFixed>(p, p.nunits, stream);
 }
 
-la_status la_prefill_fwd_varlen(const void *q, const void *k, const void *v, void *o, const int32_t *cu_seqlens,
-                                int32_t N, int32_t total_T, int32_t H, int32_t HV, int32_t D, int32_t DV,
-                                float scale, const float *slope, float *state_pool, int32_t pool_size,
-                                const int32_t *state_idx, uint32_t flags, int32_t schedule, hipStream_t stream) {
+la_status la_prefill_fwd(const void *q, const void *k, const void *v, void *o, int32_t B, int32_t T, int32_t H,
+                         int32_t HV, int32_t D, int32_t DV, float scale, const float *slope, float *state_pool,
+                         int32_t pool_size, const int32_t *state_idx, uint32_t flags, hipStream_t stream) {
+    return la_prefill_fwd_ex(q, k, v, o, B, T, H, HV, D, DV, scale, slope, state_pool, pool_size, state_idx, nullptr,
+                             flags, stream);
+}
+
+la_status la_prefill_fwd_varlen_ex(const void *q, const void *k, const void *v, void *o, const int32_t *cu_seqlens,
+                                   int32_t N, int32_t total_T, int32_t H, int32_t HV, int32_t D, int32_t DV,
+                                   float scale, const float *slope, float *state_pool, int32_t pool_size,
+                                   const int32_t *state_idx, const int32_t *state_idx_out, uint32_t flags,
+                                   int32_t schedule, hipStream_t stream) {
     clear_error();
     la_status s = check_common(H, HV, D, DV, flags, slope, state_pool, pool_size, state_idx);
     if (s != LA_OK) return s;
@@ -748,8 +765,9 @@ la_status la_prefill_fwd_varlen(const void *q, const void *k, const void *v, voi
     Params p{};
     p.q = (const uint16_t *)q; p.k = (const uint16_t *)k; p.v = (const uint16_t *)v; p.o = (uint16_t *)o;
     p.cu_seqlens = cu_seqlens; p.slope = slope; p.pool = state_pool; p.state_idx = state_idx;
+    p.state_idx_out = state_idx_out;
     p.nseq = N; p.T = 0; p.total_T = total_T; p.H = H; p.HV = HV; p.G = HV / H;
-    p.pool_size = flags ? pool_size : 0; p.npairs = N * HV; p.nunits = p.npairs * kVSplit;
+    p.pool_size = (flags & (LA_STATE_READ | LA_STATE_WRITE)) ? pool_size : 0; p.npairs = N * HV; p.nunits = p.npairs * kVSplit;
     p.scale = scale; p.flags = flags;
     int grid = p.nunits;
     if (schedule == LA_SCHED_PERSISTENT) {
@@ -762,6 +780,14 @@ la_status la_prefill_fwd_varlen(const void *q, const void *k, const void *v, voi
         grid = std::min(grid, cus);
     }
     return launch<kVarlen>(p, grid, stream);
+}
+
+la_status la_prefill_fwd_varlen(const void *q, const void *k, const void *v, void *o, const int32_t *cu_seqlens,
+                                int32_t N, int32_t total_T, int32_t H, int32_t HV, int32_t D, int32_t DV,
+                                float scale, const float *slope, float *state_pool, int32_t pool_size,
+                                const int32_t *state_idx, uint32_t flags, int32_t schedule, hipStream_t stream) {
+    return la_prefill_fwd_varlen_ex(q, k, v, o, cu_seqlens, N, total_T, H, HV, D, DV, scale, slope, state_pool,
+                                    pool_size, state_idx, nullptr, flags, schedule, stream);
 }
 
 la_status la_state_commit(const void *k, const void *v, int32_t B, int32_t T, int32_t H, int32_t HV, int32_t D,

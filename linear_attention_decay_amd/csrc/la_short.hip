@@ -37,7 +37,7 @@ struct ShortParams {
     uint16_t *kbuf, *vbuf;
     const float *slope;
     float *pool;
-    const int32_t *state_idx, *accepted_len;
+    const int32_t *state_idx, *accepted_len, *state_idx_out;
     int32_t B, T, H, HV, G, pool_size;
     float scale;
     uint32_t flags;
@@ -54,10 +54,15 @@ __global__ __launch_bounds__(kShortThreads) void la_short_kernel(ShortParams p) 
     const int lane = threadIdx.x & 63;
     const int lr = lane & 15, lg = lane >> 4;
 
-    int slot = -1;
-    if (p.flags != 0) {
+    int slot = -1, slot_out = -1;
+    if (p.flags & (LA_STATE_READ | LA_STATE_WRITE)) {
         const int s = p.state_idx[b];
         if (s >= 0 && s < p.pool_size) slot = s;
+        slot_out = slot;
+        if (p.state_idx_out) {
+            const int so = p.state_idx_out[b];
+            slot_out = (so >= 0 && so < p.pool_size) ? so : -1;
+        }
     }
     int len;
     int64_t row0;
@@ -70,14 +75,15 @@ __global__ __launch_bounds__(kShortThreads) void la_short_kernel(ShortParams p) 
         row0 = (int64_t)b * p.T;
     }
     const bool read = slot >= 0 && (p.flags & LA_STATE_READ);
-    const bool write = slot >= 0 && (p.flags & LA_STATE_WRITE);
-    const float l2 = log2_lambda(p.slope[hv]);
+    const bool write = slot_out >= 0 && (p.flags & LA_STATE_WRITE);
+    const float l2 = log2_lambda(p.slope[(p.flags & LA_DECAY_PER_QK_HEAD) ? h : hv]);
     const int qk_stride = p.H * kD * 2;                   // bytes between token rows
     const int v_stride = p.HV * kDV * 2;
     const int v0 = 32 * w;                                // first value row of this wave
 
     // ---------------------------------------------------------------- loads: state, then token rows
     float *plane = slot >= 0 ? p.pool + ((int64_t)slot * p.HV + hv) * (kDV * kD) : nullptr;
+    float *plane_out = slot_out >= 0 ? p.pool + ((int64_t)slot_out * p.HV + hv) * (kDV * kD) : nullptr;
     f32x4 S[2][8];
     if (read) {
 #pragma unroll
@@ -214,7 +220,7 @@ __global__ __launch_bounds__(kShortThreads) void la_short_kernel(ShortParams p) 
                 f32x4 s = S[vt][kt] * dec;
                 s = mfma16(kT[kt], vdh, s);
                 s = mfma16(kT[kt], vdl, s);
-                *reinterpret_cast<f32x4 *>(plane + (v0 + 16 * vt + lr) * kD + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1)) = s;
+                *reinterpret_cast<f32x4 *>(plane_out + (v0 + 16 * vt + lr) * kD + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1)) = s;
             }
         }
     }
@@ -231,7 +237,9 @@ la_status launch_short(const ShortCall &c, hipStream_t stream) {
     p.q = (const uint16_t *)c.q; p.k = (const uint16_t *)c.k; p.v = (const uint16_t *)c.v; p.o = (uint16_t *)c.o;
     p.kbuf = (uint16_t *)c.kbuf; p.vbuf = (uint16_t *)c.vbuf;
     p.slope = c.slope; p.pool = c.pool; p.state_idx = c.state_idx; p.accepted_len = c.accepted_len;
-    p.B = c.B; p.T = c.T; p.H = c.H; p.HV = c.HV; p.G = c.HV / c.H; p.pool_size = c.flags ? c.pool_size : 0;
+    p.state_idx_out = c.state_idx_out;
+    p.B = c.B; p.T = c.T; p.H = c.H; p.HV = c.HV; p.G = c.HV / c.H;
+    p.pool_size = (c.flags & (LA_STATE_READ | LA_STATE_WRITE)) ? c.pool_size : 0;
     p.scale = c.scale; p.flags = c.flags; p.rows_by_slot = c.rows_by_slot ? 1 : 0;
     if (c.commit)
         hipLaunchKernelGGL(la_short_kernel<true>, dim3(c.B * c.HV), dim3(kShortThreads), 0, stream, p);

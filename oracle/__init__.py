@@ -39,6 +39,7 @@ SRC_PATH = os.path.join(HERE, "la_oracle.c")
 
 STATE_READ = 1
 STATE_WRITE = 2
+DECAY_PER_QK_HEAD = 4
 
 _lib = None
 
@@ -179,15 +180,24 @@ def _slot_ok(idx, P):
 
 
 def prefill(q_bits, k_bits, v_bits, seq_row0, seq_len, H, HV, scale, slope, pool=None, state_idx=None,
-            flags=0, units=None):
+            flags=0, units=None, state_idx_out=None):
     """Prefill over sequences (fixed-length: row0 = b*T, len = T; packed: from cu_seqlens).
 
-    pool: float32 [P, HV, DV, D] or None; state_idx: int [nseq] or None; flags: STATE_READ | STATE_WRITE.
-    units: list of (seq, hv) to evaluate (default: all). Returns (dict (seq, hv) -> float64 [len, DV] output,
-    pool_after: float64 copy of the pool with the evaluated units' writes applied, or None).
-    A slot index < 0 or >= P means zero initial state and no write. A zero-length sequence writes its
+    pool: float32 [P, HV, DV, D] or None; state_idx: int [nseq] or None; flags: STATE_READ | STATE_WRITE
+    (| DECAY_PER_QK_HEAD). units: list of (seq, hv) to evaluate (default: all). Returns (dict (seq, hv) ->
+    float64 [len, DV] output, pool_after: float64 copy of the pool with the evaluated units' writes applied, or
+    None). A slot index < 0 or >= P means zero initial state and no write. A zero-length sequence writes its
     initial state (S0, or zero without READ) when WRITE is set.
+
+    state_idx_out (int [nseq], optional): the slot that receives sequence n's final state, in place of
+    state_idx[n] (prefill page, comparison notes: indirect / shared state-pool ownership). Every read happens
+    before any write, as when each sequence's reads and writes touch slots no other sequence writes.
+    DECAY_PER_QK_HEAD: slope has H entries, one per q/k head, and value head hv decays with slope[hv // G]
+    (prefill page, Performance: GVA rows with decay owned per q/k head, "_h"); this is the same recurrence as
+    per-value-head slopes that repeat each q/k head's slope G times.
     """
+    if flags & DECAY_PER_QK_HEAD:
+        slope = np.repeat(np.asarray(slope, np.float32), HV // H)
     nseq = len(seq_len)
     if units is None:
         units = [(n, hv) for n in range(nseq) for hv in range(HV)]
@@ -202,8 +212,9 @@ def prefill(q_bits, k_bits, v_bits, seq_row0, seq_len, H, HV, scale, slope, pool
     spec = [(int(seq_row0[n]), int(seq_len[n]), hv) for (n, hv) in units]
     outs, s_fin = tokenwise(q_bits, k_bits, v_bits, H, HV, scale, slope, spec, s0=s0, want_o=True)
     pool_after = None if pool is None else pool.astype(np.float64)
+    dst = state_idx if state_idx_out is None else state_idx_out
     for i, (n, hv) in enumerate(units):
-        s = -1 if state_idx is None else int(state_idx[n])
+        s = -1 if dst is None else int(dst[n])
         if (flags & STATE_WRITE) and pool is not None and _slot_ok(s, P):
             pool_after[s, hv] = s_fin[i]
     return {u: outs[i] for i, u in enumerate(units)}, pool_after

@@ -50,7 +50,7 @@ def _fwd(B=1, T=64, H=2, HV=2, D=128, DV=128, slope=FAKE, pool=None, P=0, idx=No
     (dict(slope=None), la.LA_ERR_INVALID_ARG),
     (dict(flags=1), la.LA_ERR_INVALID_ARG),                       # READ without pool / idx
     (dict(flags=2, pool=FAKE, P=1), la.LA_ERR_INVALID_ARG),       # WRITE without idx
-    (dict(flags=4, pool=FAKE, P=1, idx=FAKE), la.LA_ERR_INVALID_ARG),
+    (dict(flags=8, pool=FAKE, P=1, idx=FAKE), la.LA_ERR_INVALID_ARG),
     (dict(q=None), la.LA_ERR_INVALID_ARG),
     (dict(flags=3, pool=FAKE, P=-1, idx=FAKE), la.LA_ERR_INVALID_ARG),
 ])
@@ -61,6 +61,9 @@ def test_fixed_rejects_before_launch(kw, status):
 
 def test_empty_calls_are_noops():
     assert _fwd(B=0) == la.LA_OK
+    assert _fwd(B=0, flags=4) == la.LA_OK                          # per-q/k-head decay needs no pool
+    assert L.la_prefill_fwd_ex(FAKE, FAKE, FAKE, FAKE, 0, 64, 2, 2, 128, 128, 1.0, FAKE, FAKE, 1, FAKE, FAKE, 3,
+                               None) == la.LA_OK
     assert _fwd(T=0) == la.LA_OK
     assert L.la_last_error() == b""
     assert L.la_prefill_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 2, 2, 128, 128, 1.0, FAKE, None, 0, None, 0,

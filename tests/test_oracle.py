@@ -249,3 +249,49 @@ def test_bf16_rounding_matches_torch():
     mine = bf16_bits(x)
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(mine, ref)
+
+
+def test_decay_per_qk_head_matches_closed_form():
+    """With DECAY_PER_QK_HEAD the slope array has one entry per q/k head and every value head of the group decays
+    with it (prefill page, Performance: GVA rows "_h"); checked against the O(T^2) closed form per value head."""
+    rng = np.random.default_rng(23)
+    T, D, DV, H, G = 21, 16, 8, 2, 3
+    HV = H * G
+    q, k, v = _rand_unit(rng, T, D, DV, H=H, HV=HV)
+    pool = (rng.standard_normal((2, HV, DV, D)) * 0.1).astype(np.float32)
+    sl_h = np.array([0.03, 0.7], np.float32)
+    flags = oracle.STATE_READ | oracle.STATE_WRITE | oracle.DECAY_PER_QK_HEAD
+    outs, pool_after = oracle.prefill(q, k, v, [0], [T], H, HV, 0.9, sl_h, pool=pool, state_idx=[1], flags=flags)
+    qf, kf, vf = bits_to_f32(q).astype(np.float64), bits_to_f32(k).astype(np.float64), bits_to_f32(v).astype(np.float64)
+    for hv in range(HV):
+        lam = np.exp(-np.float64(sl_h[hv // G]))
+        o_ref, s_ref = oracle.closed_form(qf[:, hv // G], kf[:, hv // G], vf[:, hv], lam, 0.9,
+                                          pool[1, hv].astype(np.float64))
+        np.testing.assert_allclose(outs[(0, hv)], o_ref, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(pool_after[1, hv], s_ref, rtol=1e-11, atol=1e-12)
+
+
+def test_out_slot_relocates_the_state_and_continues():
+    """state_idx_out: the final state lands in its own slot and the read slot is untouched; reading it back
+    continues the recurrence (run(T1) -> slot 3, then run(T2) from slot 3 == run(T1 + T2) from slot 0)."""
+    rng = np.random.default_rng(29)
+    T1, T2, D, DV, H = 9, 14, 16, 8, 2
+    q, k, v = _rand_unit(rng, T1 + T2, D, DV, H=H, HV=H)
+    pool = (rng.standard_normal((5, H, DV, D)) * 0.1).astype(np.float32)
+    rw = oracle.STATE_READ | oracle.STATE_WRITE
+    sl = np.array([0.05, 0.4], np.float32)
+    _, p1 = oracle.prefill(q[:T1], k[:T1], v[:T1], [0], [T1], H, H, 1.0, sl, pool=pool, state_idx=[0], flags=rw,
+                           state_idx_out=[3])
+    for s in (0, 1, 2, 4):
+        np.testing.assert_array_equal(p1[s], pool[s].astype(np.float64))
+    o2, p2 = oracle.prefill(q[T1:], k[T1:], v[T1:], [0], [T2], H, H, 1.0, sl, pool=p1.astype(np.float32),
+                            state_idx=[3], flags=rw)
+    o_all, p_all = oracle.prefill(q, k, v, [0], [T1 + T2], H, H, 1.0, sl, pool=pool, state_idx=[0], flags=rw)
+    for hv in range(H):
+        # the relocated state passed through float32 once; agreement is at float32 rounding of S
+        np.testing.assert_allclose(o2[(0, hv)], o_all[(0, hv)][T1:], rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(p2[3, hv], p_all[0, hv], rtol=1e-5, atol=1e-6)
+    # an out slot outside the pool stores nothing
+    _, p3 = oracle.prefill(q[:T1], k[:T1], v[:T1], [0], [T1], H, H, 1.0, sl, pool=pool, state_idx=[0], flags=rw,
+                           state_idx_out=[-1])
+    np.testing.assert_array_equal(p3, pool.astype(np.float64))
