@@ -4,7 +4,8 @@ One step = one la_prefill_fwd call over the whole workload: B=2, T=8192, H=HV=64
 FP32 state read from and written back to a 2-slot pool in place (every step sees the previous step's state;
 the work per step is identical). Inputs are synthetic (la_synth recipe, seed 1) and resident in HBM before the
 timed region. Prints one JSON line. --config 0/2/3 time the other prefill workloads; --config 4 times the draft
-verify + commit chain through the KV buffer (B=128 requests, T=8).
+verify + commit chain through the KV buffer (B=128 requests, T=8); --config 5 times the segmented prefill of one
+long prompt (B=1, T=32768, H=HV=16) and reports the unsegmented time beside it.
 
   python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--config {0,1,2,3,4}]
 """
@@ -132,7 +133,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", type=int, default=1, choices=range(6))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prewarm-s", type=float, default=1.0,
                     help="untimed seconds of launches before warmup, so the timed steps run at the steady clock")
@@ -177,13 +178,25 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     chain = w.accepted_len is not None      # verify + commit of draft tokens through the KV buffer
+    seg = args.config == 5                  # one long prompt: the segmented prefill, segment count from the CUs
+    if seg:
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        n_seg = max(1, cus // (2 * w.B * w.HV))
+        ws = torch.empty(max(la.la_prefill_seg_workspace_bytes(w.B, w.HV, n_seg), 4) // 4, dtype=torch.float32,
+                         device=dev)
     if chain:
         acc = to_dev(w.accepted_len)
         kb = torch.empty((w.pool.shape[0], w.T, w.H, 128), dtype=torch.bfloat16, device=dev)
         vb = torch.empty((w.pool.shape[0], w.T, w.HV, 128), dtype=torch.bfloat16, device=dev)
 
+    def plain_step():
+        la.la_prefill_fwd(q, k, v, o, slope, scale=w.scale, state_pool=pool, state_idx=idx, flags=flags, stream=stream)
+
     def step():
-        if chain:
+        if seg:
+            la.la_prefill_fwd_seg(q, k, v, o, slope, scale=w.scale, state_pool=pool, state_idx=idx, flags=flags,
+                                  segments=0, workspace=ws, stream=stream)
+        elif chain:
             la.la_verify_kvbuffer(q, k, v, o, slope, pool, idx, k_buf=kb, v_buf=vb, scale=w.scale, stream=stream)
             la.la_state_commit_kvbuffer(kb, vb, slope, pool, idx, acc, stream=stream)
         elif cu is None:
@@ -227,11 +240,24 @@ def main():
     per = sorted(a.elapsed_time(b) for a, b in evs)
     kern_ms = sum(per) / len(per)
 
+    plain_ms = None
+    if seg:   # the same workload on the unsegmented path, for comparison
+        for _ in range(3):
+            plain_step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            plain_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        plain_ms = e0.elapsed_time(e1) / args.steps
+
     tokheads = w.tokens * w.HV
     value = tokheads / (ms_per_step * 1e-3) / 1e6
     alg_bytes = chain_bytes(w) if chain else algorithmic_bytes(w)
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    short = chain or 1 <= w.T <= 16
+    short = chain or seg or 1 <= w.T <= 16     # MFMA count below is for the plain chunked kernel only
     mfma_tfs = None if short else mfma_flops_executed(w) / (kern_ms * 1e-3) / 1e12
 
     out = {
@@ -252,7 +278,8 @@ def main():
                    "chunk": CHUNK, "state_flags": w.flags, "tokens": w.tokens},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
-                     "kernel": ("la_short_kernel<false> + la_short_kernel<true> (verify + commit)" if chain else
+                     "kernel": ("la_chunk_kernel<3> + la_seg_scan_kernel + la_chunk_kernel<4> (segmented)" if seg else
+                                "la_short_kernel<false> + la_short_kernel<true> (verify + commit)" if chain else
                                 "la_short_kernel<false>" if 1 <= w.T <= 16 else
                                 "la_chunk_kernel<1>" if cu is not None else "la_chunk_kernel<0>"),
                      "kernel_ms_avg": round(kern_ms, 6),
@@ -260,6 +287,9 @@ def main():
         "mfma": None if short else {"executed_tflops": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
                                     "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)},
     }
+    if seg:
+        out["segmented"] = {"segments_requested": n_seg, "unsegmented_ms_per_step": round(plain_ms, 6),
+                            "speedup": round(plain_ms / ms_per_step, 3)}
     if not args.no_cpu_baseline and args.config in (0, 1):
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -39,6 +39,7 @@
 #ifndef LA_PREFILL_H
 #define LA_PREFILL_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -90,6 +91,34 @@ la_status la_prefill_fwd_ex(const void *q, const void *k, const void *v, void *o
                             int32_t HV, int32_t D, int32_t DV, float scale, const float *slope, float *state_pool,
                             int32_t pool_size, const int32_t *state_idx, const int32_t *state_idx_out,
                             uint32_t flags, hipStream_t stream);
+
+/*
+ * Fixed-length prefill with every sequence split into segments processed in parallel, for calls whose
+ * (sequence, head) units cannot fill the GPU (few long sequences, few heads). Results as la_prefill_fwd_ex.
+ * The segments use the linear-attention form of the segmented scan (KDA sm90 page, Description: chunk-parallel
+ * PREP, sequential SCAN over the state):
+ *   1. each segment but the last runs from a zero state over its tokens and keeps its local state L_g;
+ *   2. a scan forms every segment's initial state, S_{g+1} = lambda^{seg_len} S_g + L_g, with S_0 the pool
+ *      state (LA_STATE_READ) or zero;
+ *   3. every segment runs the full prefill from its initial state; the last one stores the final state.
+ * segments : requested number of segments; 0 chooses one from the device's CU count (enough workgroups for
+ *            every CU, segments of at least 4 chunks). Segments are whole 64-token chunks, so fewer may be used;
+ *            with one segment, or T <= 16, the call is exactly la_prefill_fwd_ex.
+ * workspace: device buffer of at least la_prefill_seg_workspace_bytes(B, HV, segments actually used) bytes,
+ *            owned by the caller, not touched when one segment is used. la_prefill_seg_workspace_bytes(B, HV, n)
+ *            for the requested n is always enough (segments = 0: n = CU count / (2 B HV), at least 1). Calls
+ *            sharing a workspace must be ordered on one stream. Too small: LA_ERR_INVALID_ARG.
+ * Extra HBM traffic: k and v of all but the last segment are read twice, plus 3 state planes per segment.
+ */
+la_status la_prefill_fwd_seg(const void *q, const void *k, const void *v, void *o, int32_t B, int32_t T, int32_t H,
+                             int32_t HV, int32_t D, int32_t DV, float scale, const float *slope, float *state_pool,
+                             int32_t pool_size, const int32_t *state_idx, const int32_t *state_idx_out,
+                             uint32_t flags, int32_t segments, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* Workspace bytes la_prefill_fwd_seg needs for B sequences, HV value heads and the given segment count
+ * (0 for segments <= 1). */
+size_t la_prefill_seg_workspace_bytes(int32_t B, int32_t HV, int32_t segments);
 
 /*
  * Packed variable-length prefill (prefill page, Description: packed variable-length BF16 prefill; persistent

@@ -159,4 +159,8 @@ def config(i: int) -> Workload:
     if i == 4:
         # Short-chunk verify: B=128 requests, T=8 drafts, 128-slot pool; then commit accepted lengths.
         return verify(4, 128, 8, 64, 64, pool_slots=128, name="cfg4_verify_b128_t8")
+    if i == 5:
+        # One long prompt with few heads (B=1, T=32768, H=HV=16): too few (sequence, head) units to fill the GPU,
+        # the case the segmented prefill is for. State read from and written back to a 1-slot pool.
+        return fixed(5, 1, 32768, 16, 16, pool_slots=1, state_idx=[0], flags=3, name="cfg5_long_b1_t32768_h16")
     raise ValueError(i)

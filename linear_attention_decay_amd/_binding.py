@@ -15,7 +15,8 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
 LA_STATE_READ, LA_STATE_WRITE, LA_DECAY_PER_QK_HEAD = 1, 2, 4
 LA_SCHED_AUTO, LA_SCHED_PERSISTENT, LA_SCHED_NONPERSISTENT = 0, 1, 2
 
-EXPORTS = ("la_prefill_fwd", "la_prefill_fwd_ex", "la_prefill_fwd_varlen", "la_prefill_fwd_varlen_ex",
+EXPORTS = ("la_prefill_fwd", "la_prefill_fwd_ex", "la_prefill_fwd_seg", "la_prefill_seg_workspace_bytes",
+           "la_prefill_fwd_varlen", "la_prefill_fwd_varlen_ex",
            "la_state_commit", "la_decode_mtp", "la_verify_kvbuffer", "la_state_commit_kvbuffer", "la_status_string",
            "la_last_error", "la_abi_version")
 
@@ -39,6 +40,11 @@ def _load():
     L.la_prefill_fwd.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, u32, p]
     L.la_prefill_fwd_ex.restype = ctypes.c_int
     L.la_prefill_fwd_ex.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, p, u32, p]
+    L.la_prefill_fwd_seg.restype = ctypes.c_int
+    L.la_prefill_fwd_seg.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, p, u32, i32, p,
+                                     ctypes.c_size_t, p]
+    L.la_prefill_seg_workspace_bytes.restype = ctypes.c_size_t
+    L.la_prefill_seg_workspace_bytes.argtypes = [i32, i32, i32]
     L.la_prefill_fwd_varlen_ex.restype = ctypes.c_int
     L.la_prefill_fwd_varlen_ex.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, p, u32, i32,
                                            p]
@@ -259,3 +265,31 @@ def la_state_commit_kvbuffer(k_buf, v_buf, slope, state_pool, state_idx, accepte
                                         _ptr(state_pool), P, _ptr(state_idx), _ptr(accepted_len),
                                         _stream(stream, dev)))
     return state_pool
+
+
+def la_prefill_seg_workspace_bytes(B, HV, segments):
+    return int(lib.la_prefill_seg_workspace_bytes(int(B), int(HV), int(segments)))
+
+
+def la_prefill_fwd_seg(q, k, v, o, slope, scale=1.0, state_pool=None, state_idx=None, state_idx_out=None, flags=0,
+                       segments=0, workspace=None, stream=None):
+    """Fixed-length prefill with every sequence split into segments run in parallel (segments = 0: chosen from the
+    CU count). workspace: a contiguous device tensor of at least la_prefill_seg_workspace_bytes(B, HV, segments)
+    bytes (for segments = 0, of the count la_prefill_fwd_seg may choose: use la_prefill_seg_workspace_bytes with
+    max(1, CUs // (2 B HV)))."""
+    import torch
+    dev = q.device
+    B, T, H, HV, D, DV = _qkvo(q, k, v, o, dev)
+    _req(slope, "slope", torch.float32, dev)
+    _req(state_pool, "state_pool", torch.float32, dev)
+    _req(state_idx, "state_idx", torch.int32, dev)
+    _req(state_idx_out, "state_idx_out", torch.int32, dev)
+    _slope_len(slope, flags, H, HV)
+    if workspace is not None and (not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    P = 0 if state_pool is None else state_pool.shape[0]
+    _check(lib.la_prefill_fwd_seg(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, HV, D, DV, float(scale), _ptr(slope),
+                                  _ptr(state_pool), P, _ptr(state_idx), _ptr(state_idx_out), int(flags),
+                                  int(segments), _ptr(workspace), nbytes, _stream(stream, dev)))
+    return o

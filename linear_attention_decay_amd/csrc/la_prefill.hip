@@ -48,7 +48,10 @@ constexpr int kVSplit = 2;                // workgroups per (sequence, value hea
 constexpr int kVW = kDV / kVSplit;        // value columns per workgroup
 constexpr int kThreads = 512;             // 4 consumer waves (one 16-column value tile each) + 4 producer waves
 
-enum Mode { kFixed = 0, kVarlen = 1, kCommit = 2 };
+// kSegStates / kSegFwd: the two chunked passes of a sequence split into segments of seg_len tokens (unit index
+// seq = b * segments-per-sequence + g): local states of every segment but the last, from zero; then the full
+// prefill of every segment from its true initial state
+enum Mode { kFixed = 0, kVarlen = 1, kCommit = 2, kSegStates = 3, kSegFwd = 4 };
 
 struct Params {
     const uint16_t *q;
@@ -61,6 +64,9 @@ struct Params {
     float *pool;
     const int32_t *state_idx;
     const int32_t *state_idx_out;   // slot that receives the final state; NULL: the slot read from
+    float *seg_states;              // segmented passes: [B * nseg, HV, 128, 128] segment initial / local states
+    int32_t seg_len;                // segmented passes: tokens per segment (a multiple of 64)
+    int32_t nseg;                   // segmented passes: segments per sequence
     int32_t nseq;
     int32_t T;          // fixed / commit: tokens per sequence
     int32_t total_T;    // varlen: rows in q/k/v
@@ -239,7 +245,7 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
-    constexpr bool kOut = (MODE != kCommit);
+    constexpr bool kOut = (MODE != kCommit && MODE != kSegStates);
     constexpr int kStageLoads = kOut ? 10 : 6;       // buffer loads one producer wave issues per chunk
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
 
@@ -274,29 +280,60 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
         } else if (MODE == kCommit) {
             row0 = (int64_t)un.seq * p.T;
             len = min(max(p.accepted_len[un.seq], 0), p.T);
+        } else if (MODE == kSegStates || MODE == kSegFwd) {
+            const int per = (MODE == kSegStates) ? p.nseg - 1 : p.nseg;
+            const int b = un.seq / per, g = un.seq - b * per;
+            row0 = (int64_t)b * p.T + (int64_t)g * p.seg_len;
+            len = min(p.seg_len, p.T - g * p.seg_len);
         } else {
             row0 = (int64_t)un.seq * p.T;
             len = p.T;
         }
-        int slot = -1, slot_out = -1;
-        if (p.flags & (LA_STATE_READ | LA_STATE_WRITE)) {
-            const int s = p.state_idx[un.seq];
-            if (s >= 0 && s < p.pool_size) slot = s;
-            slot_out = slot;
-            if (p.state_idx_out) {
-                const int so = p.state_idx_out[un.seq];
-                slot_out = (so >= 0 && so < p.pool_size) ? so : -1;
+        // state source and destination planes of this unit (value head un.hv)
+        const float *s_in = nullptr;
+        float *s_out = nullptr;
+        {
+            constexpr int64_t kPlane = kDV * kD;
+            if (MODE == kSegStates) {
+                // local state of segment g from zero, stored as entry b * nseg + g + 1 of the segment buffer
+                const int b = un.seq / (p.nseg - 1), g = un.seq - b * (p.nseg - 1);
+                s_out = p.seg_states + ((int64_t)(b * p.nseg + g + 1) * p.HV + un.hv) * kPlane;
+            } else {
+                int bseq = un.seq, g = 0;
+                if (MODE == kSegFwd) {
+                    bseq = un.seq / p.nseg;
+                    g = un.seq - bseq * p.nseg;
+                    s_in = p.seg_states + ((int64_t)un.seq * p.HV + un.hv) * kPlane;
+                }
+                if (p.flags & (LA_STATE_READ | LA_STATE_WRITE)) {
+                    int slot = -1;
+                    const int s = p.state_idx[bseq];
+                    if (s >= 0 && s < p.pool_size) slot = s;
+                    int slot_out = slot;
+                    if (p.state_idx_out) {
+                        const int so = p.state_idx_out[bseq];
+                        slot_out = (so >= 0 && so < p.pool_size) ? so : -1;
+                    }
+                    if (MODE == kCommit) {
+                        // skipped request / L = 0: no write at all
+                        if (slot < 0 || len == 0) continue;
+                        s_in = s_out = p.pool + ((int64_t)slot * p.HV + un.hv) * kPlane;
+                    } else {
+                        if (MODE != kSegFwd && slot >= 0 && (p.flags & LA_STATE_READ))
+                            s_in = p.pool + ((int64_t)slot * p.HV + un.hv) * kPlane;
+                        if (slot_out >= 0 && (p.flags & LA_STATE_WRITE) && (MODE != kSegFwd || g == p.nseg - 1))
+                            s_out = p.pool + ((int64_t)slot_out * p.HV + un.hv) * kPlane;
+                    }
+                } else if (MODE == kCommit) {
+                    continue;
+                }
             }
         }
-        if (MODE == kCommit && (slot < 0 || len == 0)) continue;   // skipped request / L = 0: no write at all
 
         const float l2 = log2_lambda(p.slope[(p.flags & LA_DECAY_PER_QK_HEAD) ? h : un.hv]);
         const int nch = (len + kC - 1) / kC;
         const int qk_stride = p.H * kD * 2;                          // bytes between token rows
         const int v_stride = p.HV * kDV * 2;
-        float *plane = nullptr, *plane_out = nullptr;
-        if (slot >= 0) plane = p.pool + ((int64_t)slot * p.HV + un.hv) * (kDV * kD);
-        if (slot_out >= 0) plane_out = p.pool + ((int64_t)slot_out * p.HV + un.hv) * (kDV * kD);
 
         // The two roles run separate code with the same number of workgroup barriers (nch + 2 per unit), so
         // each role's loop-carried registers are allocated on their own.
@@ -311,10 +348,10 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
             float finter[4];            // scale lambda^{j+1} for j = 16jt+lr
             const float dec64 = lam_pow(l2, kC);
             const int vrow = v0 + 16 * cw + lr;
-            if (slot >= 0 && (p.flags & LA_STATE_READ)) {
+            if (s_in) {
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt)
-                    S[kt] = *reinterpret_cast<const f32x4 *>(plane + vrow * kD + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1));
+                    S[kt] = *reinterpret_cast<const f32x4 *>(s_in + vrow * kD + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1));
             } else {
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -542,10 +579,10 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                 __syncthreads();
             }
 
-            if (slot_out >= 0 && (p.flags & LA_STATE_WRITE)) {
+            if (s_out) {
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt)
-                    *reinterpret_cast<f32x4 *>(plane_out + vrow * kD + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1)) = S[kt];
+                    *reinterpret_cast<f32x4 *>(s_out + vrow * kD + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1)) = S[kt];
             }
         } else {
             // ======================================== producer: staging and scores / P
@@ -658,6 +695,49 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
         }
     }
 }
+// ---------------------------------------------------------------------------------------------------------
+// Segmented sequences: the initial state of every segment (the segmented scan over segments of the affine
+// maps S -> lambda^L S + L_g, page "linear_attention: add a Hopper (sm90) KDA prefill path", its chunk-parallel
+// PREP and sequential SCAN over the state, applied here to whole segments). Entry b * nseg of the segment
+// buffer receives sequence b's initial state (its pool slot with LA_STATE_READ, else zero); entry
+// b * nseg + g (g >= 1), which holds segment g-1's local state (from zero), becomes
+// lambda^{seg_len} * entry(g-1) + local state. One thread per 4 consecutive floats of one (sequence, head) plane.
+// ---------------------------------------------------------------------------------------------------------
+struct ScanParams {
+    const float *pool;
+    const int32_t *state_idx;
+    const float *slope;
+    float *seg_states;
+    int32_t B, HV, G, pool_size, nseg, seg_len;
+    uint32_t flags;
+};
+
+__global__ __launch_bounds__(256) void la_seg_scan_kernel(ScanParams p) {
+    constexpr int kQuads = kDV * kD / 4;                          // float4 per plane
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t plane = gid / kQuads;
+    const int e4 = (int)(gid - plane * kQuads);
+    if (plane >= (int64_t)p.B * p.HV) return;
+    const int b = (int)(plane / p.HV), hv = (int)(plane - (int64_t)b * p.HV);
+    f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (p.flags & LA_STATE_READ) {
+        const int slot = p.state_idx[b];
+        if (slot >= 0 && slot < p.pool_size)
+            st = reinterpret_cast<const f32x4 *>(p.pool + ((int64_t)slot * p.HV + hv) * (kDV * kD))[e4];
+    }
+    const float l2 = log2_lambda(p.slope[(p.flags & LA_DECAY_PER_QK_HEAD) ? hv / p.G : hv]);
+    const float dec = __builtin_amdgcn_exp2f(l2 * (float)p.seg_len);
+    f32x4 *w = reinterpret_cast<f32x4 *>(p.seg_states);
+    const int64_t stride = (int64_t)p.HV * kQuads;                // one segment entry
+    int64_t at = ((int64_t)b * p.nseg * p.HV + hv) * kQuads + e4;
+    w[at] = st;
+    for (int g = 1; g < p.nseg; ++g) {
+        at += stride;
+        st = st * dec + w[at];
+        w[at] = st;
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------------------
@@ -788,6 +868,80 @@ la_status la_prefill_fwd_varlen(const void *q, const void *k, const void *v, voi
                                 const int32_t *state_idx, uint32_t flags, int32_t schedule, hipStream_t stream) {
     return la_prefill_fwd_varlen_ex(q, k, v, o, cu_seqlens, N, total_T, H, HV, D, DV, scale, slope, state_pool,
                                     pool_size, state_idx, nullptr, flags, schedule, stream);
+}
+
+size_t la_prefill_seg_workspace_bytes(int32_t B, int32_t HV, int32_t segments) {
+    if (B <= 0 || HV <= 0 || segments <= 1) return 0;
+    return (size_t)B * (size_t)segments * (size_t)HV * (size_t)(kDV * kD) * sizeof(float);
+}
+
+la_status la_prefill_fwd_seg(const void *q, const void *k, const void *v, void *o, int32_t B, int32_t T, int32_t H,
+                             int32_t HV, int32_t D, int32_t DV, float scale, const float *slope, float *state_pool,
+                             int32_t pool_size, const int32_t *state_idx, const int32_t *state_idx_out,
+                             uint32_t flags, int32_t segments, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    clear_error();
+    la_status s = check_common(H, HV, D, DV, flags, slope, state_pool, pool_size, state_idx);
+    if (s != LA_OK) return s;
+    if (B < 0 || T < 0) return fail(LA_ERR_INVALID_ARG, "negative B or T (B=%d, T=%d)", B, T);
+    if (segments < 0) return fail(LA_ERR_INVALID_ARG, "negative segment count %d", segments);
+    const int nch = (T + kC - 1) / kC;
+    int want = segments;
+    if (want == 0) {
+        // enough segments to give every CU a workgroup, each segment at least 4 chunks long
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            int v2 = 0;
+            if (hipDeviceGetAttribute(&v2, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v2 > 0)
+                cus = v2;
+        }
+        const int64_t units = (int64_t)B * HV * kVSplit;
+        want = (int)std::max<int64_t>(1, std::min<int64_t>(nch / 4, units > 0 ? cus / units : 1));
+    }
+    want = std::max(1, std::min(want, std::max(nch, 1)));
+    const int seg_chunks = (nch + want - 1) / std::max(want, 1);
+    const int seg_len = seg_chunks * kC;
+    const int nseg = seg_len > 0 ? (T + seg_len - 1) / seg_len : 1;
+    if (B == 0 || T <= kShortMax || nseg <= 1)
+        return la_prefill_fwd_ex(q, k, v, o, B, T, H, HV, D, DV, scale, slope, state_pool, pool_size, state_idx,
+                                 state_idx_out, flags, stream);
+    if (!q || !k || !v || !o) return fail(LA_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+    if ((int64_t)B * T > INT32_MAX) return fail(LA_ERR_UNSUPPORTED, "B * T exceeds 2^31 - 1 tokens");
+    if ((int64_t)B * nseg * HV * kVSplit > INT32_MAX) return fail(LA_ERR_UNSUPPORTED, "too many segment units");
+    const size_t need = la_prefill_seg_workspace_bytes(B, HV, nseg);
+    if (!workspace || workspace_bytes < need)
+        return fail(LA_ERR_INVALID_ARG, "workspace of %zu bytes needed for %d segments (got %zu)", need, nseg,
+                    workspace ? workspace_bytes : (size_t)0);
+
+    // pass 1: local states of segments 0 .. nseg-2 from zero
+    Params p{};
+    p.k = (const uint16_t *)k; p.v = (const uint16_t *)v; p.slope = slope;
+    p.seg_states = (float *)workspace; p.seg_len = seg_len; p.nseg = nseg;
+    p.nseq = B * (nseg - 1); p.T = T; p.total_T = B * T; p.H = H; p.HV = HV; p.G = HV / H;
+    p.npairs = p.nseq * HV; p.nunits = p.npairs * kVSplit; p.scale = scale;
+    p.flags = flags & LA_DECAY_PER_QK_HEAD;
+    s = launch<kSegStates>(p, p.nunits, stream);
+    if (s != LA_OK) return s;
+
+    // scan: every segment's initial state
+    ScanParams sp{};
+    sp.pool = state_pool; sp.state_idx = state_idx; sp.slope = slope; sp.seg_states = (float *)workspace;
+    sp.B = B; sp.HV = HV; sp.G = HV / H; sp.pool_size = (flags & (LA_STATE_READ | LA_STATE_WRITE)) ? pool_size : 0;
+    sp.nseg = nseg; sp.seg_len = seg_len; sp.flags = flags;
+    const int64_t threads = (int64_t)B * HV * (kDV * kD / 4);
+    hipLaunchKernelGGL(la_seg_scan_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, sp);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(LA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+
+    // pass 2: every segment from its initial state; the last one stores the final state
+    Params f{};
+    f.q = (const uint16_t *)q; f.k = (const uint16_t *)k; f.v = (const uint16_t *)v; f.o = (uint16_t *)o;
+    f.slope = slope; f.pool = state_pool; f.state_idx = state_idx; f.state_idx_out = state_idx_out;
+    f.seg_states = (float *)workspace; f.seg_len = seg_len; f.nseg = nseg;
+    f.nseq = B * nseg; f.T = T; f.total_T = B * T; f.H = H; f.HV = HV; f.G = HV / H;
+    f.pool_size = (flags & (LA_STATE_READ | LA_STATE_WRITE)) ? pool_size : 0;
+    f.npairs = f.nseq * HV; f.nunits = f.npairs * kVSplit; f.scale = scale; f.flags = flags;
+    return launch<kSegFwd>(f, f.nunits, stream);
 }
 
 la_status la_state_commit(const void *k, const void *v, int32_t B, int32_t T, int32_t H, int32_t HV, int32_t D,

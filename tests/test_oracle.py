@@ -295,3 +295,26 @@ def test_out_slot_relocates_the_state_and_continues():
     _, p3 = oracle.prefill(q[:T1], k[:T1], v[:T1], [0], [T1], H, H, 1.0, sl, pool=pool, state_idx=[0], flags=rw,
                            state_idx_out=[-1])
     np.testing.assert_array_equal(p3, pool.astype(np.float64))
+
+
+def test_segmented_scan_reproduces_the_recurrence():
+    """Segments run from a zero state give local states L_g; the scan S_{g+1} = lambda^{Ls} S_g + L_g yields every
+    segment's initial state, and each segment run from it reproduces the full recurrence (KDA sm90 page,
+    Description: chunk-parallel PREP, sequential SCAN over the state -- here over whole segments)."""
+    rng = np.random.default_rng(37)
+    T, Ls, D, DV = 50, 12, 16, 8
+    q, k, v = _rand_unit(rng, T, D, DV)
+    s0 = rng.standard_normal((DV, D)) * 0.1
+    sl = np.array([0.08], np.float32)
+    lam = np.exp(-np.float64(sl[0]))
+    bounds = [(a, min(a + Ls, T)) for a in range(0, T, Ls)]
+    init = [s0]
+    for a, b in bounds[:-1]:
+        _, loc = oracle.tokenwise(q[a:b], k[a:b], v[a:b], 1, 1, 1.0, sl, [(0, b - a, 0)], s0=np.zeros((1, DV, D)),
+                                  want_o=False)
+        init.append(lam ** (b - a) * init[-1] + loc[0])
+    o_full, s_full = oracle.tokenwise(q, k, v, 1, 1, 0.5, sl, [(0, T, 0)], s0=s0[None])
+    for (a, b), si in zip(bounds, init):
+        o_seg, s_seg = oracle.tokenwise(q[a:b], k[a:b], v[a:b], 1, 1, 0.5, sl, [(0, b - a, 0)], s0=si[None])
+        np.testing.assert_allclose(o_seg[0], o_full[0][a:b], rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(s_seg[0], s_full[0], rtol=1e-11, atol=1e-13)
