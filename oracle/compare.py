@@ -33,6 +33,14 @@ class Accum:
         self.mx = max(self.mx, float(np.max(np.abs(e))))
         self.n += got.size
 
+    def merge(self, other):
+        """Fold in another Accum of the same comparison (e.g. a later batch of units)."""
+        self.se += other.se
+        self.sr += other.sr
+        self.mx = max(self.mx, other.mx)
+        self.n += other.n
+        return self
+
     @property
     def rel_rms(self):
         if self.sr == 0.0:

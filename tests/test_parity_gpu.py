@@ -186,37 +186,41 @@ def test_config0_tiny_full():
     assert_parity(out, st, "config 0")
 
 
-def _sample_units(w, n_seq_pick, hv_pick):
-    seqs = sorted(set(n_seq_pick))
-    return [(n, hv) for n in seqs for hv in hv_pick]
+def _all_units(w, o, pool, batch):
+    """Compare every (sequence, value head) unit with the oracle, streaming batches of units."""
+    from oracle.compare import Accum
+    units = [(n, hv) for n in range(w.nseq) for hv in range(w.HV)]
+    out, st = Accum(), Accum()
+    for i in range(0, len(units), batch):
+        a, b = compare_prefill(w, o, pool, units=units[i:i + batch])
+        out.merge(a)
+        st.merge(b)
+    return units, out, st
 
 
 @pytest.mark.slow
-def test_config1_full_size_sampled():
+def test_config1_full_size_all_units():
     w = la_synth.config(1)
     d = DevWorkload(w)
     _log("config1: running")
     o, pool = d.prefill()
     torch.cuda.synchronize()
     assert not torch.isnan(o.float()).any()
-    units = _sample_units(w, [0, 1], [0, 1, 17, 31, 46, 62, 63])
-    out, st = compare_prefill(w, o, pool, units=units)
-    _log(f"config1 sampled {len(units)} units: {out} {st}")
+    units, out, st = _all_units(w, o, pool, 32)
+    _log(f"config1 all {len(units)} units: {out} {st}")
     assert_parity(out, st, "config 1")
 
 
 @pytest.mark.slow
-def test_config2_varlen_full_size_sampled():
+def test_config2_varlen_full_size_all_units():
     w = la_synth.config(2)
     d = DevWorkload(w)
     _log(f"config2: lengths {np.diff(w.cu_seqlens).tolist()} idx {w.state_idx.tolist()}")
     o, pool = d.prefill()
     torch.cuda.synchronize()
     assert not torch.isnan(o.float()).any()
-    skipped = [n for n in range(w.nseq) if w.state_idx[n] < 0][:1]
-    units = _sample_units(w, [0, w.nseq - 1] + skipped, [0, 9, 33, 63])
-    out, st = compare_prefill(w, o, pool, units=units)
-    _log(f"config2 sampled {len(units)} units: {out} {st}")
+    units, out, st = _all_units(w, o, pool, 64)
+    _log(f"config2 all {len(units)} units: {out} {st}")
     assert_parity(out, st, "config 2")
     o2, p2 = d.prefill(schedule=la.LA_SCHED_PERSISTENT)
     torch.cuda.synchronize()
@@ -224,15 +228,14 @@ def test_config2_varlen_full_size_sampled():
 
 
 @pytest.mark.slow
-def test_config3_gva_full_size_sampled():
+def test_config3_gva_full_size_all_units():
     w = la_synth.config(3)
     d = DevWorkload(w)
     _log("config3: running")
     o, pool = d.prefill()
     torch.cuda.synchronize()
-    units = _sample_units(w, [0, 3], [0, 1, 2, 3, 30, 61, 62, 63])
-    out, st = compare_prefill(w, o, pool, units=units)
-    _log(f"config3 sampled {len(units)} units: {out} {st}")
+    units, out, st = _all_units(w, o, pool, 16)
+    _log(f"config3 all {len(units)} units: {out} {st}")
     assert_parity(out, st, "config 3")
 
 
