@@ -502,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
             };
 
             // One iteration: [output of chunk c-1] + V fragments, history term and state update of chunk c.
-            // LDS reads are issued one stage ahead of their use; scheduling fences keep the stages in order.
+            // The LDS reads of each stage are issued, into their own registers, one stage ahead of their use.
             //   kind: bit 0 = chunk c-1 has an output, bit 1 = chunk c is the short last chunk
             auto iteration = [&](int c, auto kind_tag) {
                 constexpr int kind = decltype(kind_tag)::value;
@@ -525,11 +525,9 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                 if (has_out) load_p(c - 1, pf);
                 load_v(c, va);
                 load_qk(qb, kb, 0, qf, kf);
-                __builtin_amdgcn_sched_barrier(0);
                 u32x4 shi, slo;
                 split_dec(0, dec, shi, slo);
                 if (has_out) output(c - 1, pf);
-                __builtin_amdgcn_sched_barrier(0);
                 u32x4 vdh[2], vdl[2];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
@@ -545,8 +543,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
 #pragma unroll
                         for (int x = 0; x < 4; ++x) { qf[x] = qf2[x]; kf[x] = kf2[x]; }
                     }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                    }
             };
             using K_first_last = std::integral_constant<int, 2>;
             using K_first = std::integral_constant<int, 0>;
