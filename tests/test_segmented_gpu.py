@@ -6,7 +6,7 @@ import torch
 
 import la_synth
 import linear_attention_decay_amd as la
-from gpu_util import DevWorkload, assert_parity, compare_prefill, to_dev
+from gpu_util import DevWorkload, assert_parity, bitwise_equal, compare_prefill, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -80,3 +80,36 @@ def test_segmented_rejects_small_workspace():
     ws = torch.empty(16, dtype=torch.float32, device=d.q.device)
     with pytest.raises(la.LaError):
         la.la_prefill_fwd_seg(d.q, d.k, d.v, d.new_out(), d.slope, segments=4, workspace=ws)
+
+
+def test_segmented_graph_replay_matches_eager():
+    """The three launches of the segmented prefill captured in one HIP graph and replayed, with eager work between
+    the replays, equal the eager call bitwise every time."""
+    B, T, H = 1, 1024, 2
+    w = la_synth.fixed(670, B, T, H, H, pool_slots=2, state_idx=[1], flags=3)
+    d = DevWorkload(w)
+    ws = _ws(B, H, 4, d.q.device)
+    o_ref, p_ref = d.new_out(), d.fresh_pool()
+    la.la_prefill_fwd_seg(d.q, d.k, d.v, o_ref, d.slope, state_pool=p_ref, state_idx=d.idx, flags=3, segments=4,
+                          workspace=ws)
+    torch.cuda.synchronize()
+    o, pool = d.new_out(), d.fresh_pool()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        la.la_prefill_fwd_seg(d.q, d.k, d.v, o, d.slope, state_pool=pool, state_idx=d.idx, flags=3, segments=4,
+                              workspace=ws, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        la.la_prefill_fwd_seg(d.q, d.k, d.v, o, d.slope, state_pool=pool, state_idx=d.idx, flags=3, segments=4,
+                              workspace=ws, stream=torch.cuda.current_stream())
+    for _ in range(4):
+        o.fill_(float("nan"))
+        pool.copy_(d.pool0)
+        ws.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert bitwise_equal(o, o_ref) and bitwise_equal(pool, p_ref)

@@ -183,3 +183,41 @@ def test_config4_kvbuffer_chain_full():
     _log(f"config4 KV-buffer chain: verify {out} commit {st}")
     assert_parity(out, None, "config 4 verify (KV buffer)")
     assert st.rel_rms <= STATE_REL_RMS
+
+
+def test_kvbuffer_chain_graph_replay_matches_eager():
+    """verify + commit through the KV buffer captured in one HIP graph and replayed, with eager work between the
+    replays, equals the eager chain bitwise every time."""
+    w = la_synth.verify(170, 16, 8, 2, 4, pool_slots=20)
+    d = DevWorkload(w)
+
+    def chain(o, pool, kb, vb, stream):
+        la.la_verify_kvbuffer(d.q, d.k, d.v, o, d.slope, pool, d.idx, k_buf=kb, v_buf=vb, scale=w.scale,
+                              stream=stream)
+        la.la_state_commit_kvbuffer(kb, vb, d.slope, pool, d.idx, d.acc, stream=stream)
+
+    o_ref, p_ref = d.new_out(), d.fresh_pool()
+    kb_ref, vb_ref = _kv_buffers(w, d, 0.0)
+    chain(o_ref, p_ref, kb_ref, vb_ref, None)
+    torch.cuda.synchronize()
+    o, pool = d.new_out(), d.fresh_pool()
+    kb, vb = _kv_buffers(w, d, 0.0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        chain(o, pool, kb, vb, s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain(o, pool, kb, vb, torch.cuda.current_stream())
+    for _ in range(4):
+        o.fill_(float("nan"))
+        pool.copy_(d.pool0)
+        kb.zero_()
+        vb.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert bitwise_equal(o, o_ref) and bitwise_equal(pool, p_ref)
+        assert bitwise_equal(kb, kb_ref) and bitwise_equal(vb, vb_ref)
