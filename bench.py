@@ -80,11 +80,16 @@ TRAFFIC = {   # workload -> (committed FETCH_SIZE / WRITE_SIZE summary, kernel s
 
 
 def kernel_source_sha(names):
-    """sha256 over the concatenated kernel sources (the key a traffic summary records)."""
+    """sha256 over the concatenated kernel sources with comments and whitespace removed (the key a traffic
+    summary records: editing a comment does not change the kernel the counters were taken on)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for n in names:
-        h.update(open(os.path.join(CSRC, n), "rb").read())
+        src = open(os.path.join(CSRC, n)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update("".join(src.split()).encode())
     return h.hexdigest()
 
 

@@ -1,4 +1,5 @@
-// la_prefill.hip -- Lightning Attention chunked prefill for AMD Instinct MI355X (gfx950, CDNA4).
+// la_prefill.hip -- Lightning Attention chunked prefill for AMD Instinct MI355X (gfx950, CDNA4), and the C ABI
+// entry points of the prefill, commit and segmented calls.
 //
 // Computes, per (sequence, value head), the decayed linear-attention recurrence
 //     S_t = lambda S_{t-1} + v_t k_t^T,   o_t = scale S_t q_t,   lambda = exp(-slope[hv])
@@ -12,7 +13,9 @@
 // Work decomposition: one workgroup = (sequence, value head, half of the 128 value columns), 8 wave64s. The 4
 // consumer waves each own value columns [16w, 16w+16) of the half: the state rows S[v][0..127] for those
 // columns stay in that wave's registers as MFMA accumulators for the whole sequence. The 4 producer waves
-// stage Q, K, V tiles into LDS and compute the decay-masked intra-chunk scores.
+// stage Q, K, V tiles into LDS two chunks ahead, compute the decay-masked intra-chunk scores and store the
+// output tiles the consumers leave in LDS. The same kernel also runs the two chunked passes of a sequence split
+// into segments (local segment states from zero; every segment from its initial state).
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16, FP32 accumulate). Every operand fragment a lane holds is
 // "row r = lane % 16, slot group g = lane / 16, 8 slots"; slots 0..3 carry contraction indices 4g..4g+3 of
@@ -20,8 +23,8 @@
 // instruction holds, per lane, column lane % 16 and rows 4g..4g+3. Chaining works because an accumulator
 // tile [m][n] is, lane for lane, a fragment with row n and contraction index m: scores computed as
 // A^T[i][j] feed the P.V product as P[j][i] fragments; the state kept as S^T[k][v] feeds Q.S^T as S[v][k]
-// fragments; and K, V rows are turned into K^T, V^T fragments with one 16x16x16 MFMA against the identity
-// (exact: a single nonzero product per output).
+// fragments. K^T fragments come from transposing LDS reads (ds_read_b64_tr_b16) and V^T fragments from one
+// 16x16x16 MFMA against the identity (exact: a single nonzero product per output).
 //
 // Precision: the state update multiplies the per-token decay into V (V_dec = lambda^{Lc-1-i} v_i) in FP32
 // and feeds it as a bf16 hi + lo pair; the FP32 state enters Q S^T as a bf16 hi + lo pair; the decay-masked
@@ -107,7 +110,7 @@ __device__ __forceinline__ Unit decode_unit(int u, const Params &p) {
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// LDS layout (one workgroup per CU; 144 KiB).
+// LDS layout (one workgroup per CU; 160 KiB).
 //   Q, K tiles: 64 rows x 256 B; V tiles (one value half): 64 rows x 128 B. Row-major as in HBM, with the
 //   16-byte segments of row r stored at segment index seg XOR (r % 16) for Q, seg XOR f(r % 16) for K
 //   (f swaps the two 2-bit halves of its argument) and seg XOR ((r/2) % 8) for V. LDS serves a 16-byte read
