@@ -31,6 +31,7 @@
  *     out of bounds. Slopes must be >= 0 (+inf is allowed and means lambda = 0).
  *   - Host-checkable problems return an error before anything is enqueued:
  *       D != 128, DV != 128, H <= 0, HV % H != 0            -> LA_ERR_UNSUPPORTED
+ *       HV > 65536 (row strides are 32-bit byte offsets)  -> LA_ERR_UNSUPPORTED
  *       negative sizes, NULL required pointer, bad flags     -> LA_ERR_INVALID_ARG
  *     A NULL state_pool / state_idx is allowed when flags holds neither LA_STATE_READ nor LA_STATE_WRITE.
  *     A call with no tokens and no sequences is a successful no-op. A launch failure returns LA_ERR_HIP.

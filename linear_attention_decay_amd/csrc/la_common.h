@@ -71,6 +71,8 @@ la_status check_common(int32_t H, int32_t HV, int32_t D, int32_t DV, uint32_t fl
 
 // short-sequence path (T <= kShortMax), implemented next to its kernel
 constexpr int kShortMax = 16;
+// largest value-head count: a chunk's 64 token rows of HV * 256 bytes are addressed with 32-bit offsets
+constexpr int kMaxHeads = 65536;
 struct ShortCall {
     const void *q, *k, *v;       // token rows [B, T, H|HV, 128]; for a commit from a KV buffer, rows of slot s
     void *o;                     // output [B, T, HV, 128], or NULL when no output is produced

@@ -765,6 +765,9 @@ la_status check_common(int32_t H, int32_t HV, int32_t D, int32_t DV, uint32_t fl
         return fail(LA_ERR_UNSUPPORTED, "head counts must be positive (H=%d, HV=%d)", H, HV);
     if (HV % H != 0)
         return fail(LA_ERR_UNSUPPORTED, "HV (%d) must be a multiple of H (%d)", HV, H);
+    // the kernels address a chunk's rows with 32-bit byte offsets: 63 rows of HV * 256 bytes must stay < 2^31
+    if (HV > kMaxHeads)
+        return fail(LA_ERR_UNSUPPORTED, "at most %d value heads are supported (got HV=%d)", kMaxHeads, HV);
     if (flags & ~(uint32_t)(LA_STATE_READ | LA_STATE_WRITE | LA_DECAY_PER_QK_HEAD))
         return fail(LA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
     if (!slope) return fail(LA_ERR_INVALID_ARG, "slope is NULL");

@@ -45,6 +45,7 @@ def _fwd(B=1, T=64, H=2, HV=2, D=128, DV=128, slope=FAKE, pool=None, P=0, idx=No
     (dict(H=3, HV=4), la.LA_ERR_UNSUPPORTED),
     (dict(H=4, HV=2), la.LA_ERR_UNSUPPORTED),
     (dict(H=0, HV=0), la.LA_ERR_UNSUPPORTED),
+    (dict(H=1, HV=65537), la.LA_ERR_UNSUPPORTED),                # 32-bit row offsets
     (dict(B=-1), la.LA_ERR_INVALID_ARG),
     (dict(T=-5), la.LA_ERR_INVALID_ARG),
     (dict(slope=None), la.LA_ERR_INVALID_ARG),
