@@ -74,6 +74,10 @@ CSRC = os.path.join(ROOT, "linear_attention_decay_amd", "csrc")
 TRAFFIC = {   # workload -> (committed FETCH_SIZE / WRITE_SIZE summary, kernel sources it was measured on)
     1: (os.path.join(ROOT, "profiles", "la_chunk_kernel_fixed_b2_t8192_h64_hbm_traffic.md"),
         ("la_common.h", "la_prefill.hip")),
+    2: (os.path.join(ROOT, "profiles", "la_chunk_kernel_varlen_n16_h64_hbm_traffic.md"),
+        ("la_common.h", "la_prefill.hip")),
+    3: (os.path.join(ROOT, "profiles", "la_chunk_kernel_gva_b4_t16384_h16_hv64_hbm_traffic.md"),
+        ("la_common.h", "la_prefill.hip")),
     4: (os.path.join(ROOT, "profiles", "la_short_kernel_verify_commit_b128_t8_h64_hbm_traffic.md"),
         ("la_common.h", "la_short.hip")),
 }

@@ -87,24 +87,32 @@ struct Unit {
     int32_t seq, hv, vpart;
 };
 
-// Workgroup -> (pair, value half). Pairs are handed out in groups of 8 so that the two halves of a pair
-// sit 8 workgroups apart: workgroups are dealt round-robin over the 8 XCDs, so both halves of one
-// (sequence, head) land on the same XCD and share its L2 for the Q/K rows they both read.
+// Workgroup -> (sequence, value head, value half). The units that read the same Q/K rows -- the G value heads
+// of one (sequence, q/k head) group, times the two value halves -- get indices 8 apart: workgroups are dealt
+// round-robin over the 8 XCDs, so the whole group lands on one XCD, in consecutive dispatch slots, and shares
+// that XCD's L2 for the Q/K tiles. Groups are dealt over the XCDs in rows of 8; a last partial row of m groups
+// interleaves its units over all XCDs.
 __device__ __forceinline__ Unit decode_unit(int u, const Params &p) {
-    const int full = p.npairs >> 3;
-    int pair, half;
-    if ((u >> 4) < full) {
-        pair = (u >> 4) * 8 + (u & 7);
-        half = (u >> 3) & 1;
+    const int per = kVSplit * p.G;           // units per group
+    const int ngroups = p.npairs / p.G;      // nseq * H
+    const int full = ngroups >> 3;           // complete rows of 8 groups
+    int group, j;
+    if (u < full * 8 * per) {
+        const int slot = u >> 3;             // dispatch slot on XCD u % 8
+        const int row = slot / per;
+        group = row * 8 + (u & 7);
+        j = slot - row * per;
     } else {
-        const int m = p.npairs - full * 8;
-        const int r = u - full * 16;
-        pair = full * 8 + r % m;
-        half = r / m;
+        const int m = ngroups - full * 8;
+        const int r = u - full * 8 * per;
+        group = full * 8 + r % m;
+        j = r / m;
     }
+    const int half = j / p.G;
+    const int seq = group / p.H;
     Unit t;
-    t.seq = pair / p.HV;
-    t.hv = pair - t.seq * p.HV;
+    t.seq = seq;
+    t.hv = (group - seq * p.H) * p.G + (j - half * p.G);
     t.vpart = half;
     return t;
 }
