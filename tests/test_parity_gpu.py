@@ -36,6 +36,21 @@ def test_fixed_sweep(T, G):
     assert_parity(out, st, f"T={T} G={G}")
 
 
+@pytest.mark.parametrize("B,H,G", [(1, 11, 2), (3, 3, 4), (2, 8, 3)])
+def test_gva_groups_full_rows_and_tail(B, H, G):
+    """Workgroups are dealt to (sequence, q/k head) groups in rows of 8 groups plus a last partial row: 11 and 9
+    groups take both branches, 16 groups only full rows; every unit of every group is checked (o is NaN-poisoned,
+    so a unit left out would show)."""
+    w = la_synth.fixed(300 + 10 * H + G, B, 130, H, H * G, pool_slots=B + 1, state_idx=list(range(B)), flags=3)
+    w.slope = (np.linspace(0.0, 0.5, H * G) ** 2).astype(np.float32)
+    _log(f"gva groups B={B} H={H} G={G}")
+    d = DevWorkload(w)
+    o, pool = d.prefill()
+    torch.cuda.synchronize()
+    out, st = compare_prefill(w, o, pool)
+    assert_parity(out, st, f"B={B} H={H} G={G}")
+
+
 @pytest.mark.parametrize("flags", [0, 1, 2, 3])
 def test_state_flags(flags):
     w = la_synth.fixed(7, 3, 130, 2, 4, pool_slots=5, state_idx=[4, -1, 1], flags=flags)
