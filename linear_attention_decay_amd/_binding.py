@@ -98,9 +98,26 @@ def _req(t, name, dtype, dev):
 
 
 def _slope_len(slope, flags, H, HV):
+    if slope is None:
+        raise ValueError("slope is required")
     want = H if flags & LA_DECAY_PER_QK_HEAD else HV
     if slope.numel() != want:
         raise ValueError(f"slope must have {want} entries, got {slope.numel()}")
+
+
+def _state_shapes(state_pool, HV, n, required=False, **idx):
+    """The kernels index the pool as [P, HV, 128, 128] and read one entry of every index tensor per sequence: check
+    the shapes here, since the library cannot see allocation sizes."""
+    if state_pool is None:
+        if required:
+            raise ValueError("state_pool is required")
+        return 0
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (HV, 128, 128):
+        raise ValueError(f"state_pool must have shape [P, {HV}, 128, 128], got {tuple(state_pool.shape)}")
+    for name, t in idx.items():
+        if t is not None and t.numel() != n:
+            raise ValueError(f"{name} must have {n} entries, got {t.numel()}")
+    return state_pool.shape[0]
 
 
 def la_prefill_fwd(q, k, v, o, slope, scale=1.0, state_pool=None, state_idx=None, flags=0, stream=None,
@@ -122,7 +139,7 @@ def la_prefill_fwd(q, k, v, o, slope, scale=1.0, state_pool=None, state_idx=None
     if k.shape != q.shape or v.shape[:2] != (B, T) or o.shape != v.shape:
         raise ValueError("shape mismatch between q, k, v, o")
     _slope_len(slope, flags, H, HV)
-    P = 0 if state_pool is None else state_pool.shape[0]
+    P = _state_shapes(state_pool, HV, B, state_idx=state_idx)
     _check(lib.la_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, HV, D, DV, float(scale), _ptr(slope),
                               _ptr(state_pool), P, _ptr(state_idx), int(flags), _stream(stream, dev)))
     return o
@@ -139,7 +156,7 @@ def la_prefill_fwd_ex(q, k, v, o, slope, scale=1.0, state_pool=None, state_idx=N
     _req(state_idx, "state_idx", torch.int32, dev)
     _req(state_idx_out, "state_idx_out", torch.int32, dev)
     _slope_len(slope, flags, H, HV)
-    P = 0 if state_pool is None else state_pool.shape[0]
+    P = _state_shapes(state_pool, HV, B, state_idx=state_idx, state_idx_out=state_idx_out)
     _check(lib.la_prefill_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, HV, D, DV, float(scale), _ptr(slope),
                                  _ptr(state_pool), P, _ptr(state_idx), _ptr(state_idx_out), int(flags),
                                  _stream(stream, dev)))
@@ -164,8 +181,10 @@ def la_prefill_fwd_varlen(q, k, v, o, cu_seqlens, slope, scale=1.0, state_pool=N
         raise ValueError("shape mismatch between q, k, v, o")
     _req(state_idx_out, "state_idx_out", torch.int32, dev)
     _slope_len(slope, flags, H, HV)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 offsets")
     N = cu_seqlens.shape[0] - 1
-    P = 0 if state_pool is None else state_pool.shape[0]
+    P = _state_shapes(state_pool, HV, N, state_idx=state_idx, state_idx_out=state_idx_out)
     if state_idx_out is None:
         _check(lib.la_prefill_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens), N, total_T, H, HV, D,
                                          DV, float(scale), _ptr(slope), _ptr(state_pool), P, _ptr(state_idx),
@@ -196,8 +215,12 @@ def la_state_commit(k, v, slope, state_pool, state_idx, accepted_len, stream=Non
     _req(accepted_len, "accepted_len", torch.int32, dev)
     B, T, H, D = k.shape
     HV, DV = v.shape[2], v.shape[3]
+    if v.shape[:2] != (B, T):
+        raise ValueError("shape mismatch between k and v")
+    _slope_len(slope, 0, H, HV)
+    P = _state_shapes(state_pool, HV, B, required=True, state_idx=state_idx, accepted_len=accepted_len)
     _check(lib.la_state_commit(_ptr(k), _ptr(v), B, T, H, HV, D, DV, _ptr(slope), _ptr(state_pool),
-                               state_pool.shape[0], _ptr(state_idx), _ptr(accepted_len), _stream(stream, dev)))
+                               P, _ptr(state_idx), _ptr(accepted_len), _stream(stream, dev)))
     return state_pool
 
 
@@ -220,8 +243,10 @@ def la_decode_mtp(q, k, v, o, slope, state_pool, state_idx, scale=1.0, stream=No
     _req(slope, "slope", torch.float32, dev)
     _req(state_pool, "state_pool", torch.float32, dev)
     _req(state_idx, "state_idx", torch.int32, dev)
+    _slope_len(slope, 0, H, HV)
+    P = _state_shapes(state_pool, HV, B, required=True, state_idx=state_idx)
     _check(lib.la_decode_mtp(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, HV, D, DV, float(scale), _ptr(slope),
-                             _ptr(state_pool), state_pool.shape[0], _ptr(state_idx), _stream(stream, dev)))
+                             _ptr(state_pool), P, _ptr(state_idx), _stream(stream, dev)))
     return o
 
 
@@ -234,7 +259,8 @@ def la_verify_kvbuffer(q, k, v, o, slope, state_pool, state_idx, k_buf=None, v_b
     _req(slope, "slope", torch.float32, dev)
     _req(state_pool, "state_pool", torch.float32, dev)
     _req(state_idx, "state_idx", torch.int32, dev)
-    P = state_pool.shape[0]
+    _slope_len(slope, 0, H, HV)
+    P = _state_shapes(state_pool, HV, B, required=True, state_idx=state_idx)
     for t, n, heads in ((k_buf, "k_buf", H), (v_buf, "v_buf", HV)):
         _req(t, n, torch.bfloat16, dev)
         if t is not None and tuple(t.shape) != (P, T, heads, 128):
@@ -258,9 +284,13 @@ def la_state_commit_kvbuffer(k_buf, v_buf, slope, state_pool, state_idx, accepte
     _req(accepted_len, "accepted_len", torch.int32, dev)
     P, T, H, D = k_buf.shape
     HV, DV = v_buf.shape[2], v_buf.shape[3]
-    if v_buf.shape[:2] != (P, T) or state_pool.shape[0] != P:
+    if v_buf.shape[:2] != (P, T) or state_pool is None or state_pool.shape[0] != P:
         raise ValueError("k_buf, v_buf and state_pool must share the slot count and T")
-    B = state_idx.shape[0]
+    if state_idx is None or accepted_len is None:
+        raise ValueError("state_idx and accepted_len are required")
+    B = state_idx.numel()
+    _slope_len(slope, 0, H, HV)
+    _state_shapes(state_pool, HV, B, required=True, state_idx=state_idx, accepted_len=accepted_len)
     _check(lib.la_state_commit_kvbuffer(_ptr(k_buf), _ptr(v_buf), B, T, H, HV, D, DV, _ptr(slope),
                                         _ptr(state_pool), P, _ptr(state_idx), _ptr(accepted_len),
                                         _stream(stream, dev)))
@@ -288,7 +318,7 @@ def la_prefill_fwd_seg(q, k, v, o, slope, scale=1.0, state_pool=None, state_idx=
     if workspace is not None and (not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous tensor on the device of q")
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    P = 0 if state_pool is None else state_pool.shape[0]
+    P = _state_shapes(state_pool, HV, B, state_idx=state_idx, state_idx_out=state_idx_out)
     _check(lib.la_prefill_fwd_seg(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, HV, D, DV, float(scale), _ptr(slope),
                                   _ptr(state_pool), P, _ptr(state_idx), _ptr(state_idx_out), int(flags),
                                   int(segments), _ptr(workspace), nbytes, _stream(stream, dev)))
