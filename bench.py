@@ -7,7 +7,7 @@ timed region. Prints one JSON line. --config 0/2/3 time the other prefill worklo
 verify + commit chain through the KV buffer (B=128 requests, T=8); --config 5 times the segmented prefill of one
 long prompt (B=1, T=32768, H=HV=16) and reports the unsegmented time beside it.
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--config {0,1,2,3,4}]
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--config {0,1,2,3,4,5}]
 """
 from __future__ import annotations
 
@@ -152,7 +152,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
-              f"multi-GPU sharding in this build)", file=sys.stderr)
+              f"sharding over several GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

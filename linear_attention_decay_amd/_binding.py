@@ -33,7 +33,7 @@ def _load():
     # pointers and streams are not torch's. Import torch before dlopen so the soname is already satisfied.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"HIP library not built: {LIB_PATH} is missing; run __graft_entry__.build()")
+        raise ImportError(f"HIP library not built: {LIB_PATH} is missing; build it with python linear_attention_decay_amd/build.py")
     L = ctypes.CDLL(LIB_PATH)
     p, i32, u32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float
     L.la_prefill_fwd.restype = ctypes.c_int
