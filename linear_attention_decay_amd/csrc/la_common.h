@@ -66,6 +66,9 @@ __device__ __forceinline__ float log2_lambda(float slope) {
 // makes before it enqueues anything
 void clear_error();
 la_status fail(la_status s, const char *fmt, ...);
+// compute units of the current device (cached per device; 256 if the query fails)
+int cu_count();
+
 la_status check_common(int32_t H, int32_t HV, int32_t D, int32_t DV, uint32_t flags, const float *slope,
                        const float *pool, int32_t pool_size, const int32_t *state_idx);
 

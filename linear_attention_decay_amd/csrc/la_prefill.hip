@@ -35,6 +35,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <stdio.h>
 #include <stdarg.h>
@@ -757,6 +758,21 @@ thread_local char g_err[512] = "";
 
 void clear_error() { g_err[0] = 0; }
 
+int cu_count() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    if (dev >= 0 && dev < kMaxDevices) cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
 la_status fail(la_status s, const char *fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
@@ -861,15 +877,7 @@ la_status la_prefill_fwd_varlen_ex(const void *q, const void *k, const void *v, 
     p.pool_size = (flags & (LA_STATE_READ | LA_STATE_WRITE)) ? pool_size : 0; p.npairs = N * HV; p.nunits = p.npairs * kVSplit;
     p.scale = scale; p.flags = flags;
     int grid = p.nunits;
-    if (schedule == LA_SCHED_PERSISTENT) {
-        int dev = 0, cus = 256;
-        if (hipGetDevice(&dev) == hipSuccess) {
-            int v2 = 0;
-            if (hipDeviceGetAttribute(&v2, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v2 > 0)
-                cus = v2;
-        }
-        grid = std::min(grid, cus);
-    }
+    if (schedule == LA_SCHED_PERSISTENT) grid = std::min(grid, cu_count());
     return launch<kVarlen>(p, grid, stream);
 }
 
@@ -900,12 +908,7 @@ la_status la_prefill_fwd_seg(const void *q, const void *k, const void *v, void *
     int want = segments;
     if (want == 0) {
         // enough segments to give every CU a workgroup, each segment at least 4 chunks long
-        int dev = 0, cus = 256;
-        if (hipGetDevice(&dev) == hipSuccess) {
-            int v2 = 0;
-            if (hipDeviceGetAttribute(&v2, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v2 > 0)
-                cus = v2;
-        }
+        const int cus = cu_count();
         const int64_t units = (int64_t)B * HV * kVSplit;
         want = (int)std::max<int64_t>(1, std::min<int64_t>(nch / 4, units > 0 ? cus / units : 1));
     }

@@ -9,8 +9,11 @@
 // used by verify, and the state-update / commit kernel). Both are computed straight from S0 in one pass, with
 // no intermediate states.
 //
-// Work decomposition: one workgroup of 4 wave64s per (request, value head); wave w owns value rows
-// [32w, 32w+32) of the state, held as 2 x 8 tiles of MFMA accumulators (tile kt: lane (lr, lg) holds
+// Work decomposition: wave w of a (request, value head) unit owns value rows [32w, 32w+32) of the state; value rows
+// never interact, so the 4 waves of a unit are independent. They run as one 4-wave workgroup per unit, or, when
+// there are fewer units than compute units (small-batch decode), as 4 one-wave workgroups per unit so that the
+// state loads spread over 4 times as many CUs (the launch picks the form). Each wave holds its rows as 2 x 8 tiles
+// of MFMA accumulators (tile kt: lane (lr, lg) holds
 // S[v = 32w + 16vt + lr][k] for the keys k = kappa(kt, lg, r) = 32(kt/2) + 8lg + 4(kt%2) + r). The state is
 // the dominant HBM traffic (64 KiB per request and head); each lane loads and stores it in 16-byte pieces.
 //
@@ -42,15 +45,17 @@ struct ShortParams {
     float scale;
     uint32_t flags;
     int32_t rows_by_slot;
+    int32_t wave_units;         // 1: one-wave workgroups, 4 per unit (blockIdx = 4 unit + wave)
 };
 
 template <bool kCommitMode>
 __global__ __launch_bounds__(kShortThreads) void la_short_kernel(ShortParams p) {
     constexpr bool kOut = !kCommitMode;
-    const int b = blockIdx.x / p.HV;
-    const int hv = blockIdx.x - b * p.HV;
+    const int unit = p.wave_units ? (int)(blockIdx.x >> 2) : (int)blockIdx.x;
+    const int b = unit / p.HV;
+    const int hv = unit - b * p.HV;
     const int h = hv / p.G;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int w = p.wave_units ? (int)(blockIdx.x & 3) : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int lr = lane & 15, lg = lane >> 4;
 
@@ -232,7 +237,7 @@ namespace la_detail {
 
 la_status launch_short(const ShortCall &c, hipStream_t stream) {
     if (c.T > kShortMax || c.T <= 0) return fail(LA_ERR_UNSUPPORTED, "short path takes 1 <= T <= %d (T=%d)", kShortMax, c.T);
-    if ((int64_t)c.B * c.HV > INT32_MAX) return fail(LA_ERR_UNSUPPORTED, "too many (request, head) units");
+    if ((int64_t)c.B * c.HV * 4 > INT32_MAX) return fail(LA_ERR_UNSUPPORTED, "too many (request, head) units");
     ShortParams p{};
     p.q = (const uint16_t *)c.q; p.k = (const uint16_t *)c.k; p.v = (const uint16_t *)c.v; p.o = (uint16_t *)c.o;
     p.kbuf = (uint16_t *)c.kbuf; p.vbuf = (uint16_t *)c.vbuf;
@@ -241,10 +246,14 @@ la_status launch_short(const ShortCall &c, hipStream_t stream) {
     p.B = c.B; p.T = c.T; p.H = c.H; p.HV = c.HV; p.G = c.HV / c.H;
     p.pool_size = (c.flags & (LA_STATE_READ | LA_STATE_WRITE)) ? c.pool_size : 0;
     p.scale = c.scale; p.flags = c.flags; p.rows_by_slot = c.rows_by_slot ? 1 : 0;
+    // work units: with fewer (request, head) units than CUs, one-wave workgroups reach 4x as many CUs
+    const int units = c.B * c.HV;
+    p.wave_units = units < cu_count() ? 1 : 0;
+    const dim3 grid(p.wave_units ? 4 * units : units), block(p.wave_units ? 64 : kShortThreads);
     if (c.commit)
-        hipLaunchKernelGGL(la_short_kernel<true>, dim3(c.B * c.HV), dim3(kShortThreads), 0, stream, p);
+        hipLaunchKernelGGL(la_short_kernel<true>, grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL(la_short_kernel<false>, dim3(c.B * c.HV), dim3(kShortThreads), 0, stream, p);
+        hipLaunchKernelGGL(la_short_kernel<false>, grid, block, 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(LA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return LA_OK;

@@ -65,6 +65,33 @@ def test_decode_mtp_matches_prefill_read_write():
     assert_parity(out, st, "decode_mtp")
 
 
+@pytest.mark.parametrize("extra", [-1, 0])
+def test_work_unit_forms_on_both_sides_of_the_cu_count(extra):
+    """Fewer (request, head) units than CUs run as four one-wave workgroups per unit, otherwise as one four-wave
+    workgroup per unit: decode with CUs - 1 and CUs units checks both forms, with every unit against the oracle,
+    and the KV-buffer copy of verify (written by wave 0 of a unit) bitwise."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    units = cus + extra
+    HV = 8 if units % 8 == 0 else 1
+    B = units // HV
+    w = la_synth.fixed(95 + extra, B, 8, HV, HV, pool_slots=B + 1, state_idx=list(range(B, 0, -1)), flags=3,
+                       scale=0.7)
+    _log(f"work units: {B} requests x {HV} heads = {B * HV} units, {cus} CUs")
+    d = DevWorkload(w)
+    o, pool = d.new_out(), d.fresh_pool()
+    la.la_decode_mtp(d.q, d.k, d.v, o, d.slope, pool, d.idx, scale=w.scale)
+    torch.cuda.synchronize()
+    out, st = compare_prefill(w, o, pool, flags=3)
+    assert_parity(out, st, f"{B * HV} units")
+    kb = torch.zeros(B + 1, 8, HV, 128, dtype=torch.bfloat16, device=d.q.device)
+    vb = torch.zeros_like(kb)
+    o2 = d.new_out()
+    la.la_verify_kvbuffer(d.q, d.k, d.v, o2, d.slope, d.fresh_pool(), d.idx, k_buf=kb, v_buf=vb, scale=w.scale)
+    torch.cuda.synchronize()
+    slots = torch.as_tensor(w.state_idx, device=d.q.device).long()
+    assert bitwise_equal(kb[slots], d.k) and bitwise_equal(vb[slots], d.v)
+
+
 def test_decode_mtp_two_steps_continue_the_recurrence():
     # decode 5 drafts, then 3 more from the updated pool == the 8-token recurrence
     w = la_synth.fixed(92, 3, 8, 2, 2, pool_slots=3, state_idx=[2, 0, 1], flags=3)
