@@ -7,7 +7,7 @@ import torch
 
 import linear_attention_decay_amd as la
 import oracle
-from oracle.compare import OUT_MAX_ABS, OUT_REL_RMS, STATE_REL_RMS, Accum
+from oracle.compare import OUT_MAX_ABS, OUT_REL_RMS, STATE_REL_RMS, Accum, within
 
 DEV = torch.device("cuda:0")
 
@@ -84,7 +84,7 @@ def compare_prefill(w, o_dev, pool_dev, units=None, flags=None, scale=None):
     out = Accum()
     for (n, hv), ref in ref_o.items():
         r0, L = rows[n]
-        out.add(got[r0:r0 + L, hv], ref)
+        out.add(got[r0:r0 + L, hv], ref, unit=(n, hv))
     st = Accum()
     if pool_dev is not None:
         pool_got = pool_dev.cpu().numpy()
@@ -103,15 +103,38 @@ def compare_prefill(w, o_dev, pool_dev, units=None, flags=None, scale=None):
             s = int(w.state_idx[n]) if w.state_idx is not None else -1
             if (flags & la.LA_STATE_WRITE) and 0 <= s < P and (s, hv) not in checked:
                 checked.add((s, hv))
-                st.add(pool_got[s, hv], ref_pool[s, hv])
+                st.add(pool_got[s, hv], ref_pool[s, hv], unit=(s, hv))
     return out, st
 
 
 def assert_parity(out, st=None, what=""):
-    assert out.rel_rms <= OUT_REL_RMS, f"{what} output rel RMS {out.rel_rms:.3e} > {OUT_REL_RMS}"
-    assert out.max_abs <= OUT_MAX_ABS, f"{what} output max abs {out.max_abs:.3e} > {OUT_MAX_ABS}"
+    """Joint bars over the whole call, then the same relative-RMS bar for every unit the Accums name (a (sequence,
+    value head) output unit, a (slot, value head) state plane). NaN fails every bar."""
+    assert within(out.rel_rms, OUT_REL_RMS), f"{what} output rel RMS {out.rel_rms:.3e} > {OUT_REL_RMS}"
+    assert within(out.max_abs, OUT_MAX_ABS), f"{what} output max abs {out.max_abs:.3e} > {OUT_MAX_ABS}"
+    w = out.worst_unit()
+    if w is not None:
+        assert within(w[1], OUT_REL_RMS), f"{what} output unit {w[0]} rel RMS {w[1]:.3e} > {OUT_REL_RMS}"
     if st is not None and st.n:
-        assert st.rel_rms <= STATE_REL_RMS, f"{what} state rel RMS {st.rel_rms:.3e} > {STATE_REL_RMS}"
+        assert within(st.rel_rms, STATE_REL_RMS), f"{what} state rel RMS {st.rel_rms:.3e} > {STATE_REL_RMS}"
+        w = st.worst_unit()
+        if w is not None:
+            assert within(w[1], STATE_REL_RMS), f"{what} state plane {w[0]} rel RMS {w[1]:.3e} > {STATE_REL_RMS}"
+
+
+def add_state_slot(st, got, ref, slot):
+    """Add the HV planes of one pool slot to a state Accum, one unit per (slot, value head) plane."""
+    for hv in range(ref.shape[0]):
+        st.add(got[hv], ref[hv], unit=(slot, hv))
+
+
+def assert_state(st, what=""):
+    """Final-state bar, jointly and per plane."""
+    assert st.n, f"{what}: no state compared"
+    assert within(st.rel_rms, STATE_REL_RMS), f"{what} state rel RMS {st.rel_rms:.3e} > {STATE_REL_RMS}"
+    w = st.worst_unit()
+    if w is not None:
+        assert within(w[1], STATE_REL_RMS), f"{what} state plane {w[0]} rel RMS {w[1]:.3e} > {STATE_REL_RMS}"
 
 
 def bitwise_equal(a, b):

@@ -12,7 +12,7 @@ import torch
 import la_synth
 import linear_attention_decay_amd as la
 import oracle
-from gpu_util import DevWorkload, assert_parity, bitwise_equal, to_dev
+from gpu_util import DevWorkload, add_state_slot, assert_parity, bitwise_equal, to_dev
 from oracle.compare import Accum
 
 pytestmark = pytest.mark.gpu
@@ -27,14 +27,14 @@ def _compare(w, o_dev, pool_dev, flags, idx_out, slope):
     out = Accum()
     for (n, hv), ref in ref_o.items():
         r0, L = rows[n]
-        out.add(got[r0:r0 + L, hv], ref)
+        out.add(got[r0:r0 + L, hv], ref, unit=(n, hv))
     st = Accum()
     pool_got = pool_dev.cpu().numpy()
     P = w.pool.shape[0]
     written = {int(s) for s in idx_out if 0 <= int(s) < P} if flags & la.LA_STATE_WRITE else set()
     for s in range(P):
         if s in written:
-            st.add(pool_got[s], ref_pool[s])
+            add_state_slot(st, pool_got[s], ref_pool[s], s)
         else:
             assert np.array_equal(pool_got[s].view(np.uint32), w.pool[s].view(np.uint32)), f"slot {s} touched"
     return out, st

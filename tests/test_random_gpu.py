@@ -9,8 +9,8 @@ import torch
 import la_synth
 import linear_attention_decay_amd as la
 import oracle
-from gpu_util import DevWorkload, assert_parity, compare_prefill, to_dev
-from oracle.compare import STATE_REL_RMS, Accum
+from gpu_util import DevWorkload, add_state_slot, assert_parity, assert_state, compare_prefill, to_dev
+from oracle.compare import Accum
 
 pytestmark = pytest.mark.gpu
 
@@ -70,13 +70,13 @@ def test_random_segmented_with_options(case):
     out = Accum()
     for (n, hv), ref in ref_o.items():
         r0, L = rows[n]
-        out.add(got[r0:r0 + L, hv], ref)
+        out.add(got[r0:r0 + L, hv], ref, unit=(n, hv))
     st = Accum()
     pg = pool.cpu().numpy()
     written = {int(s) for s in idx_out if s >= 0} if fl & la.LA_STATE_WRITE else set()
     for s in range(pg.shape[0]):
         if s in written:
-            st.add(pg[s], ref_pool[s])
+            add_state_slot(st, pg[s], ref_pool[s], s)
         else:
             assert np.array_equal(pg[s].view(np.uint32), w.pool[s].view(np.uint32)), f"slot {s} touched"
     assert_parity(out, st, f"seg case {case}")
@@ -109,7 +109,7 @@ def test_random_varlen_and_commit(case):
     for b in range(v.B):
         s = int(v.state_idx[b])
         if v.accepted_len[b] > 0:
-            st.add(got[s], ref[s])
+            add_state_slot(st, got[s], ref[s], s)
         else:
             assert np.array_equal(got[s].view(np.uint32), v.pool[s].view(np.uint32))
-    assert st.rel_rms <= STATE_REL_RMS, f"commit case {case}: {st}"
+    assert_state(st, f"commit case {case}")

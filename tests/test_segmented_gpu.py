@@ -6,7 +6,7 @@ import torch
 
 import la_synth
 import linear_attention_decay_amd as la
-from gpu_util import DevWorkload, assert_parity, bitwise_equal, compare_prefill, to_dev
+from gpu_util import DevWorkload, add_state_slot, assert_parity, bitwise_equal, compare_prefill, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -65,10 +65,10 @@ def test_segmented_auto_out_slots_and_qk_decay():
     got = o.float().cpu().numpy().reshape(-1, H * G, 128)
     out = Accum()
     for (n, hv), ref in ref_o.items():
-        out.add(got[:, hv], ref)
+        out.add(got[:, hv], ref, unit=(n, hv))
     st = Accum()
     pg = pool.cpu().numpy()
-    st.add(pg[2], ref_pool[2])
+    add_state_slot(st, pg[2], ref_pool[2], 2)
     for s in (0, 1):
         assert np.array_equal(pg[s].view(np.uint32), w.pool[s].view(np.uint32))
     assert_parity(out, st, "segmented auto")

@@ -12,8 +12,8 @@ import torch
 import la_synth
 import linear_attention_decay_amd as la
 import oracle
-from gpu_util import DevWorkload, assert_parity, bitwise_equal, compare_prefill, to_dev
-from oracle.compare import STATE_REL_RMS, Accum
+from gpu_util import DevWorkload, add_state_slot, assert_parity, assert_state, bitwise_equal, compare_prefill, to_dev
+from oracle.compare import Accum
 
 pytestmark = pytest.mark.gpu
 
@@ -179,12 +179,12 @@ def test_commit_kvbuffer_against_oracle_and_direct_commit(T, G):
         s = int(w.state_idx[b])
         if 0 <= s < w.pool.shape[0] and w.accepted_len[b] > 0:
             written.add(s)
-            st.add(got[s], ref[s])
+            add_state_slot(st, got[s], ref[s], s)
     for s in range(w.pool.shape[0]):
         if s not in written:
             assert np.array_equal(got[s].view(np.uint32), w.pool[s].view(np.uint32)), f"slot {s} written"
     _log(f"commit_kvbuffer T={T} G={G}: {st}")
-    assert st.rel_rms <= STATE_REL_RMS
+    assert_state(st, "commit")
 
 
 def test_config4_kvbuffer_chain_full():
@@ -206,10 +206,10 @@ def test_config4_kvbuffer_chain_full():
         if w.accepted_len[b] == 0:
             assert np.array_equal(got[s].view(np.uint32), w.pool[s].view(np.uint32))
         else:
-            st.add(got[s], ref[s])
+            add_state_slot(st, got[s], ref[s], s)
     _log(f"config4 KV-buffer chain: verify {out} commit {st}")
     assert_parity(out, None, "config 4 verify (KV buffer)")
-    assert st.rel_rms <= STATE_REL_RMS
+    assert_state(st, "commit")
 
 
 def test_kvbuffer_chain_graph_replay_matches_eager():
