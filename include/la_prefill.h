@@ -117,6 +117,31 @@ la_status la_prefill_fwd_seg(const void *q, const void *k, const void *v, void *
                              uint32_t flags, int32_t segments, void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/*
+ * la_prefill_fwd_seg without a workspace argument, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Arguments, results and errors as
+ * la_prefill_fwd_seg. The per-segment states live in a fixed device array of the library instead of a caller
+ * workspace:
+ *   - its size is la_prefill_seg_noalloc_max_bytes() (16 MiB: B * segments * HV <= 256 state planes); a call
+ *     whose segment count needs more returns LA_ERR_UNSUPPORTED before anything is enqueued (choose fewer
+ *     segments, or use la_prefill_fwd_seg with a workspace). segments = 0 on a 256-CU device always fits;
+ *   - every device that runs the library holds one copy until the process ends; its address is looked up once
+ *     per device (the first call on a device), the only runtime call besides the launches;
+ *   - this call allocates and frees nothing, and nothing in the array has to start at zero: each call writes
+ *     every entry it reads before reading it;
+ *   - all calls on one device share the array, so calls that overlap in time on one device (different streams
+ *     without ordering between them) race and give undefined results; order them on one stream.
+ * Calls that need one segment (or T <= 16) do not touch the array.
+ */
+la_status la_prefill_fwd_seg_noalloc(const void *q, const void *k, const void *v, void *o, int32_t B, int32_t T,
+                                     int32_t H, int32_t HV, int32_t D, int32_t DV, float scale, const float *slope,
+                                     float *state_pool, int32_t pool_size, const int32_t *state_idx,
+                                     const int32_t *state_idx_out, uint32_t flags, int32_t segments,
+                                     hipStream_t stream);
+
+/* Bytes of the fixed device array la_prefill_fwd_seg_noalloc uses (its largest segment workspace). */
+size_t la_prefill_seg_noalloc_max_bytes(void);
+
 /* Workspace bytes la_prefill_fwd_seg needs for B sequences, HV value heads and the given segment count
  * (0 for segments <= 1). */
 size_t la_prefill_seg_workspace_bytes(int32_t B, int32_t HV, int32_t segments);

@@ -20,6 +20,8 @@ from ._binding import (  # noqa: F401
     la_prefill_fwd,
     la_prefill_fwd_ex,
     la_prefill_fwd_seg,
+    la_prefill_fwd_seg_noalloc,
+    la_prefill_seg_noalloc_max_bytes,
     la_prefill_seg_workspace_bytes,
     la_prefill_fwd_varlen,
     la_prefill_fwd_varlen_ex,

@@ -16,6 +16,7 @@ LA_STATE_READ, LA_STATE_WRITE, LA_DECAY_PER_QK_HEAD = 1, 2, 4
 LA_SCHED_AUTO, LA_SCHED_PERSISTENT, LA_SCHED_NONPERSISTENT = 0, 1, 2
 
 EXPORTS = ("la_prefill_fwd", "la_prefill_fwd_ex", "la_prefill_fwd_seg", "la_prefill_seg_workspace_bytes",
+           "la_prefill_fwd_seg_noalloc", "la_prefill_seg_noalloc_max_bytes",
            "la_prefill_fwd_varlen", "la_prefill_fwd_varlen_ex",
            "la_state_commit", "la_decode_mtp", "la_verify_kvbuffer", "la_state_commit_kvbuffer", "la_status_string",
            "la_last_error", "la_abi_version")
@@ -43,6 +44,11 @@ def _load():
     L.la_prefill_fwd_seg.restype = ctypes.c_int
     L.la_prefill_fwd_seg.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, p, u32, i32, p,
                                      ctypes.c_size_t, p]
+    L.la_prefill_fwd_seg_noalloc.restype = ctypes.c_int
+    L.la_prefill_fwd_seg_noalloc.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, i32, p, p, u32, i32,
+                                             p]
+    L.la_prefill_seg_noalloc_max_bytes.restype = ctypes.c_size_t
+    L.la_prefill_seg_noalloc_max_bytes.argtypes = []
     L.la_prefill_seg_workspace_bytes.restype = ctypes.c_size_t
     L.la_prefill_seg_workspace_bytes.argtypes = [i32, i32, i32]
     L.la_prefill_fwd_varlen_ex.restype = ctypes.c_int
@@ -322,4 +328,27 @@ def la_prefill_fwd_seg(q, k, v, o, slope, scale=1.0, state_pool=None, state_idx=
     _check(lib.la_prefill_fwd_seg(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, HV, D, DV, float(scale), _ptr(slope),
                                   _ptr(state_pool), P, _ptr(state_idx), _ptr(state_idx_out), int(flags),
                                   int(segments), _ptr(workspace), nbytes, _stream(stream, dev)))
+    return o
+
+
+def la_prefill_seg_noalloc_max_bytes():
+    return int(lib.la_prefill_seg_noalloc_max_bytes())
+
+
+def la_prefill_fwd_seg_noalloc(q, k, v, o, slope, scale=1.0, state_pool=None, state_idx=None, state_idx_out=None,
+                               flags=0, segments=0, stream=None):
+    """la_prefill_fwd_seg with the segment states in the library's fixed device array: no workspace and no
+    allocation. Calls that overlap on one device race on that array."""
+    import torch
+    dev = q.device
+    B, T, H, HV, D, DV = _qkvo(q, k, v, o, dev)
+    _req(slope, "slope", torch.float32, dev)
+    _req(state_pool, "state_pool", torch.float32, dev)
+    _req(state_idx, "state_idx", torch.int32, dev)
+    _req(state_idx_out, "state_idx_out", torch.int32, dev)
+    _slope_len(slope, flags, H, HV)
+    P = _state_shapes(state_pool, HV, B, state_idx=state_idx, state_idx_out=state_idx_out)
+    _check(lib.la_prefill_fwd_seg_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, H, HV, D, DV, float(scale),
+                                          _ptr(slope), _ptr(state_pool), P, _ptr(state_idx), _ptr(state_idx_out),
+                                          int(flags), int(segments), _stream(stream, dev)))
     return o

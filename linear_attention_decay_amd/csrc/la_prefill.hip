@@ -36,6 +36,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <stdio.h>
 #include <stdarg.h>
@@ -813,6 +814,122 @@ la_status launch(const Params &p, int grid, hipStream_t stream) {
     return LA_OK;
 }
 
+
+// Device scratch of la_prefill_fwd_seg_noalloc: the per-segment state buffer of the segmented prefill, in a fixed
+// array of kScratchBytes that every device running the library holds until the process ends. Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for the symbol); it uses the device
+// address that hipGetSymbolAddress returns for the current device, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)16 << 20;      // 256 state planes of 64 KiB
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+la_status scratch_address(hipStream_t stream, void **out) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void *> addr[kMaxDevices];
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return fail(LA_ERR_HIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(LA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (p) {
+        *out = p;
+        return LA_OK;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        // the symbol's address is per device: look it up with the stream's device current
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return fail(LA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(LA_ERR_HIP, "hipSetDevice(%d) failed: %s", dev, hipGetErrorString(e));
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t e2 = (cur != dev) ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess || !p)
+            return fail(LA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+        if (e2 != hipSuccess) return fail(LA_ERR_HIP, "hipSetDevice(%d) failed: %s", cur, hipGetErrorString(e2));
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return LA_OK;
+}
+
+// The segmented prefill behind la_prefill_fwd_seg (caller's workspace) and la_prefill_fwd_seg_noalloc (the
+// device scratch above). Every workspace entry a kernel reads was written earlier in the same call, so nothing
+// has to be cleared first.
+la_status seg_prefill(const void *q, const void *k, const void *v, void *o, int32_t B, int32_t T, int32_t H,
+                      int32_t HV, int32_t D, int32_t DV, float scale, const float *slope, float *state_pool,
+                      int32_t pool_size, const int32_t *state_idx, const int32_t *state_idx_out, uint32_t flags,
+                      int32_t segments, void *workspace, size_t workspace_bytes, bool use_scratch,
+                      hipStream_t stream) {
+    clear_error();
+    la_status s = check_common(H, HV, D, DV, flags, slope, state_pool, pool_size, state_idx);
+    if (s != LA_OK) return s;
+    if (B < 0 || T < 0) return fail(LA_ERR_INVALID_ARG, "negative B or T (B=%d, T=%d)", B, T);
+    if (segments < 0) return fail(LA_ERR_INVALID_ARG, "negative segment count %d", segments);
+    const int nch = (T + kC - 1) / kC;
+    int want = segments;
+    if (want == 0) {
+        // enough segments to give every CU a workgroup, each segment at least 4 chunks long
+        const int cus = cu_count();
+        const int64_t units = (int64_t)B * HV * kVSplit;
+        want = (int)std::max<int64_t>(1, std::min<int64_t>(nch / 4, units > 0 ? cus / units : 1));
+    }
+    want = std::max(1, std::min(want, std::max(nch, 1)));
+    const int seg_chunks = (nch + want - 1) / std::max(want, 1);
+    const int seg_len = seg_chunks * kC;
+    const int nseg = seg_len > 0 ? (T + seg_len - 1) / seg_len : 1;
+    if (B == 0 || T <= kShortMax || nseg <= 1)
+        return la_prefill_fwd_ex(q, k, v, o, B, T, H, HV, D, DV, scale, slope, state_pool, pool_size, state_idx,
+                                 state_idx_out, flags, stream);
+    if (!q || !k || !v || !o) return fail(LA_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+    if ((int64_t)B * T > INT32_MAX) return fail(LA_ERR_UNSUPPORTED, "B * T exceeds 2^31 - 1 tokens");
+    if ((int64_t)B * nseg * HV * kVSplit > INT32_MAX) return fail(LA_ERR_UNSUPPORTED, "too many segment units");
+    const size_t need = la_prefill_seg_workspace_bytes(B, HV, nseg);
+    if (use_scratch) {
+        if (need > kScratchBytes)
+            return fail(LA_ERR_UNSUPPORTED,
+                        "%d segments of B=%d sequences and HV=%d heads need %zu bytes of scratch; the allocation-free "
+                        "call holds at most %zu (B * segments * HV <= %zu state planes)",
+                        nseg, B, HV, need, kScratchBytes, kScratchBytes / ((size_t)kDV * kD * sizeof(float)));
+        s = scratch_address(stream, &workspace);
+        if (s != LA_OK) return s;
+    } else if (!workspace || workspace_bytes < need) {
+        return fail(LA_ERR_INVALID_ARG, "workspace of %zu bytes needed for %d segments (got %zu)", need, nseg,
+                    workspace ? workspace_bytes : (size_t)0);
+    }
+
+    // pass 1: local states of segments 0 .. nseg-2 from zero
+    Params p{};
+    p.k = (const uint16_t *)k; p.v = (const uint16_t *)v; p.slope = slope;
+    p.seg_states = (float *)workspace; p.seg_len = seg_len; p.nseg = nseg;
+    p.nseq = B * (nseg - 1); p.T = T; p.total_T = B * T; p.H = H; p.HV = HV; p.G = HV / H;
+    p.npairs = p.nseq * HV; p.nunits = p.npairs * kVSplit; p.scale = scale;
+    p.flags = flags & LA_DECAY_PER_QK_HEAD;
+    s = launch<kSegStates>(p, p.nunits, stream);
+    if (s != LA_OK) return s;
+
+    // scan: every segment's initial state
+    ScanParams sp{};
+    sp.pool = state_pool; sp.state_idx = state_idx; sp.slope = slope; sp.seg_states = (float *)workspace;
+    sp.B = B; sp.HV = HV; sp.G = HV / H; sp.pool_size = (flags & (LA_STATE_READ | LA_STATE_WRITE)) ? pool_size : 0;
+    sp.nseg = nseg; sp.seg_len = seg_len; sp.flags = flags;
+    const int64_t threads = (int64_t)B * HV * (kDV * kD / 4);
+    hipLaunchKernelGGL(la_seg_scan_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, sp);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(LA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+
+    // pass 2: every segment from its initial state; the last one stores the final state
+    Params f{};
+    f.q = (const uint16_t *)q; f.k = (const uint16_t *)k; f.v = (const uint16_t *)v; f.o = (uint16_t *)o;
+    f.slope = slope; f.pool = state_pool; f.state_idx = state_idx; f.state_idx_out = state_idx_out;
+    f.seg_states = (float *)workspace; f.seg_len = seg_len; f.nseg = nseg;
+    f.nseq = B * nseg; f.T = T; f.total_T = B * T; f.H = H; f.HV = HV; f.G = HV / H;
+    f.pool_size = (flags & (LA_STATE_READ | LA_STATE_WRITE)) ? pool_size : 0;
+    f.npairs = f.nseq * HV; f.nunits = f.npairs * kVSplit; f.scale = scale; f.flags = flags;
+    return launch<kSegFwd>(f, f.nunits, stream);
+}
 }  // namespace
 
 extern "C" {
@@ -899,64 +1016,20 @@ la_status la_prefill_fwd_seg(const void *q, const void *k, const void *v, void *
                              int32_t pool_size, const int32_t *state_idx, const int32_t *state_idx_out,
                              uint32_t flags, int32_t segments, void *workspace, size_t workspace_bytes,
                              hipStream_t stream) {
-    clear_error();
-    la_status s = check_common(H, HV, D, DV, flags, slope, state_pool, pool_size, state_idx);
-    if (s != LA_OK) return s;
-    if (B < 0 || T < 0) return fail(LA_ERR_INVALID_ARG, "negative B or T (B=%d, T=%d)", B, T);
-    if (segments < 0) return fail(LA_ERR_INVALID_ARG, "negative segment count %d", segments);
-    const int nch = (T + kC - 1) / kC;
-    int want = segments;
-    if (want == 0) {
-        // enough segments to give every CU a workgroup, each segment at least 4 chunks long
-        const int cus = cu_count();
-        const int64_t units = (int64_t)B * HV * kVSplit;
-        want = (int)std::max<int64_t>(1, std::min<int64_t>(nch / 4, units > 0 ? cus / units : 1));
-    }
-    want = std::max(1, std::min(want, std::max(nch, 1)));
-    const int seg_chunks = (nch + want - 1) / std::max(want, 1);
-    const int seg_len = seg_chunks * kC;
-    const int nseg = seg_len > 0 ? (T + seg_len - 1) / seg_len : 1;
-    if (B == 0 || T <= kShortMax || nseg <= 1)
-        return la_prefill_fwd_ex(q, k, v, o, B, T, H, HV, D, DV, scale, slope, state_pool, pool_size, state_idx,
-                                 state_idx_out, flags, stream);
-    if (!q || !k || !v || !o) return fail(LA_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
-    if ((int64_t)B * T > INT32_MAX) return fail(LA_ERR_UNSUPPORTED, "B * T exceeds 2^31 - 1 tokens");
-    if ((int64_t)B * nseg * HV * kVSplit > INT32_MAX) return fail(LA_ERR_UNSUPPORTED, "too many segment units");
-    const size_t need = la_prefill_seg_workspace_bytes(B, HV, nseg);
-    if (!workspace || workspace_bytes < need)
-        return fail(LA_ERR_INVALID_ARG, "workspace of %zu bytes needed for %d segments (got %zu)", need, nseg,
-                    workspace ? workspace_bytes : (size_t)0);
-
-    // pass 1: local states of segments 0 .. nseg-2 from zero
-    Params p{};
-    p.k = (const uint16_t *)k; p.v = (const uint16_t *)v; p.slope = slope;
-    p.seg_states = (float *)workspace; p.seg_len = seg_len; p.nseg = nseg;
-    p.nseq = B * (nseg - 1); p.T = T; p.total_T = B * T; p.H = H; p.HV = HV; p.G = HV / H;
-    p.npairs = p.nseq * HV; p.nunits = p.npairs * kVSplit; p.scale = scale;
-    p.flags = flags & LA_DECAY_PER_QK_HEAD;
-    s = launch<kSegStates>(p, p.nunits, stream);
-    if (s != LA_OK) return s;
-
-    // scan: every segment's initial state
-    ScanParams sp{};
-    sp.pool = state_pool; sp.state_idx = state_idx; sp.slope = slope; sp.seg_states = (float *)workspace;
-    sp.B = B; sp.HV = HV; sp.G = HV / H; sp.pool_size = (flags & (LA_STATE_READ | LA_STATE_WRITE)) ? pool_size : 0;
-    sp.nseg = nseg; sp.seg_len = seg_len; sp.flags = flags;
-    const int64_t threads = (int64_t)B * HV * (kDV * kD / 4);
-    hipLaunchKernelGGL(la_seg_scan_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, sp);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(LA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-
-    // pass 2: every segment from its initial state; the last one stores the final state
-    Params f{};
-    f.q = (const uint16_t *)q; f.k = (const uint16_t *)k; f.v = (const uint16_t *)v; f.o = (uint16_t *)o;
-    f.slope = slope; f.pool = state_pool; f.state_idx = state_idx; f.state_idx_out = state_idx_out;
-    f.seg_states = (float *)workspace; f.seg_len = seg_len; f.nseg = nseg;
-    f.nseq = B * nseg; f.T = T; f.total_T = B * T; f.H = H; f.HV = HV; f.G = HV / H;
-    f.pool_size = (flags & (LA_STATE_READ | LA_STATE_WRITE)) ? pool_size : 0;
-    f.npairs = f.nseq * HV; f.nunits = f.npairs * kVSplit; f.scale = scale; f.flags = flags;
-    return launch<kSegFwd>(f, f.nunits, stream);
+    return seg_prefill(q, k, v, o, B, T, H, HV, D, DV, scale, slope, state_pool, pool_size, state_idx, state_idx_out,
+                       flags, segments, workspace, workspace_bytes, false, stream);
 }
+
+la_status la_prefill_fwd_seg_noalloc(const void *q, const void *k, const void *v, void *o, int32_t B, int32_t T,
+                                     int32_t H, int32_t HV, int32_t D, int32_t DV, float scale, const float *slope,
+                                     float *state_pool, int32_t pool_size, const int32_t *state_idx,
+                                     const int32_t *state_idx_out, uint32_t flags, int32_t segments,
+                                     hipStream_t stream) {
+    return seg_prefill(q, k, v, o, B, T, H, HV, D, DV, scale, slope, state_pool, pool_size, state_idx, state_idx_out,
+                       flags, segments, nullptr, 0, true, stream);
+}
+
+size_t la_prefill_seg_noalloc_max_bytes(void) { return kScratchBytes; }
 
 la_status la_state_commit(const void *k, const void *v, int32_t B, int32_t T, int32_t H, int32_t HV, int32_t D,
                           int32_t DV, const float *slope, float *state_pool, int32_t pool_size,

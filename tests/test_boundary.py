@@ -1,6 +1,5 @@
-"""Host-side checks of the C-ABI library (no GPU): it loads, exports every declared symbol, and rejects
-host-checkable problems before enqueuing anything (prefill page, Description: unsupported specialisations
-fail explicitly rather than silently falling back)."""
+"""Host-side checks of the C-ABI library (no GPU): it loads, exports every declared symbol, and answers every
+problem it can see on the host with an error status before it enqueues anything (prefill page, Description)."""
 import ctypes
 import os
 import re
@@ -112,6 +111,20 @@ def test_short_path_entry_points_reject_before_launch():
     assert c(FAKE, FAKE, 2, 8, 2, 2, 128, 128, FAKE, FAKE, 4, FAKE, None, None) == la.LA_ERR_INVALID_ARG
     assert c(FAKE, FAKE, 2, 8, 3, 2, 128, 128, FAKE, FAKE, 4, FAKE, FAKE, None) == la.LA_ERR_UNSUPPORTED
     assert c(FAKE, FAKE, 2, 0, 2, 2, 128, 128, FAKE, FAKE, 4, FAKE, FAKE, None) == la.LA_OK
+
+
+def test_seg_noalloc_refuses_beyond_its_array_before_launch():
+    f = L.la_prefill_fwd_seg_noalloc
+    assert L.la_prefill_seg_noalloc_max_bytes() == 16 << 20
+    # 1 sequence x 8 segments x 64 heads = 512 state planes of 64 KiB > 16 MiB
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1024, 64, 64, 128, 128, 1.0, FAKE, None, 0, None, None, 0, 8, None) == \
+        la.LA_ERR_UNSUPPORTED
+    assert b"scratch" in L.la_last_error()
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1024, 2, 2, 128, 128, 1.0, FAKE, None, 0, None, None, 0, -1, None) == \
+        la.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1024, 2, 2, 64, 128, 1.0, FAKE, None, 0, None, None, 0, 4, None) == \
+        la.LA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 1024, 2, 2, 128, 128, 1.0, FAKE, None, 0, None, None, 0, 4, None) == la.LA_OK
 
 
 def test_python_binding_rejects_bad_tensors():
