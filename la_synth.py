@@ -26,9 +26,20 @@ S0_STD = 0.1
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 -> bf16 with round-to-nearest-even; returns uint16 bit patterns (finite inputs)."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    r = ((u >> 16) & 1) + np.uint32(0x7FFF)
-    return ((u + r) >> 16).astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).reshape(-1)
+    out = np.empty(u.shape, dtype=np.uint16)
+    blk = 1 << 22                      # in cache-sized blocks: large inputs are tens of millions of elements
+    r = np.empty(min(blk, u.size), dtype=np.uint32)
+    for a in range(0, u.size, blk):
+        ub = u[a:a + blk]
+        rb = r[:ub.size]
+        np.right_shift(ub, 16, out=rb)
+        np.bitwise_and(rb, 1, out=rb)
+        rb += np.uint32(0x7FFF)
+        rb += ub
+        rb >>= 16
+        out[a:a + ub.size] = rb
+    return out.reshape(np.shape(x))
 
 
 def bits_to_f32(bits: np.ndarray) -> np.ndarray:

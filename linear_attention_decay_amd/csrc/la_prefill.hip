@@ -256,23 +256,35 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
 }
 
+// Passes every field of the parameters through an empty asm, so that values derived from them count as
+// computed anew wherever the copy is made.
+__device__ __forceinline__ void opaque_params(Params &p) {
+    asm volatile("" : "+s"(p.q), "+s"(p.k), "+s"(p.v), "+s"(p.o), "+s"(p.cu_seqlens), "+s"(p.accepted_len));
+    asm volatile("" : "+s"(p.slope), "+s"(p.pool), "+s"(p.state_idx), "+s"(p.state_idx_out), "+s"(p.seg_states));
+    asm volatile("" : "+s"(p.seg_len), "+s"(p.nseg), "+s"(p.nseq), "+s"(p.T), "+s"(p.total_T), "+s"(p.H), "+s"(p.HV),
+                 "+s"(p.G), "+s"(p.pool_size), "+s"(p.npairs), "+s"(p.nunits), "+s"(p.scale), "+s"(p.flags));
+}
+
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
+__global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
     constexpr bool kOut = (MODE != kCommit && MODE != kSegStates);
     constexpr int kStageLoads = kOut ? 10 : 6;       // buffer loads one producer wave issues per chunk
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
 
     const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform: role branches are scalar
-    const bool consumer = w < 4;
-    const int cw = w & 3;            // consumer: value tile; producer: producer index
 
-    for (int u = blockIdx.x; u < p.nunits; u += gridDim.x) {
-        // Lane indices are re-derived through an opaque copy in every unit iteration so that the compiler
-        // does not hoist lane-dependent set-up (decay exponents, masks) of both roles out of this loop and
-        // keep it live for the whole kernel.
+    for (int u = blockIdx.x; u < params.nunits; u += gridDim.x) {
+        // The parameters, lane and wave indices are re-derived through opaque copies in every unit iteration,
+        // so that the compiler does not hoist set-up derived from them (decay exponents, masks, addresses, the
+        // LDS destinations of the staging loads) out of this loop for both roles and keep it live in registers
+        // for the whole kernel.
+        Params p = params;
+        opaque_params(p);
         int tid_u = tid;
         asm volatile("" : "+v"(tid_u));
+        const int w = __builtin_amdgcn_readfirstlane(tid_u >> 6);   // wave index, uniform: role branches are scalar
+        const bool consumer = w < 4;
+        const int cw = w & 3;            // consumer: value tile; producer: producer index
         const int lane = tid_u & 63;
         const int lr = lane & 15;
         const int lg = lane >> 4;
@@ -357,7 +369,6 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
             // chosen (through the transposing K reads that build the K^T fragments) so that tiles 2s and 2s+1
             // give each lane 8 consecutive keys -- the slot layout of a plain 16-byte Q row read.
             f32x4 S[8];
-            float fvd64[16];            // lambda^{63-i} for i = 16it+4lg+r (full chunk)
             float finter[4];            // scale lambda^{j+1} for j = 16jt+lr
             const float dec64 = lam_pow(l2, kC);
             const int vrow = v0 + 16 * cw + lr;
@@ -369,27 +380,37 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-#pragma unroll
-            for (int it = 0; it < 4; ++it)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) fvd64[4 * it + r] = lam_pow(l2, 63 - (16 * it + 4 * lg + r));
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt) finter[jt] = p.scale * lam_pow(l2, 16 * jt + lr + 1);
+            float fvd64[16];            // V_dec factors of a full chunk, lambda^{63-i} for i = 16it+4lg+r
             s16x4 ident;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ident[e] = (4 * lg + e == lr) ? (short)0x3F80 : (short)0;
             // per-lane LDS offsets reused by every chunk: Q fragment (row lr, segment 4s + lg; row tile jt adds
             // 4096 B); V^T source (row lr, value tile cw; token tile it adds 2048 B); K^T source of key group s:
             // lane (lg, lr) supplies token row 4lg + lr/4 (+ 32 per token pair, + 16 for slots 4..7) and the 4
             // keys 32s + 8(lr%4) + 4kk .. +3; the transposing read hands lane lr of each 16-lane group key
-            // kappa(2s + kk, lr) = 32s + 8(lr/4) + 4kk + lr%4 of the 4 rows of its group.
-            int q_off[4], tr_off[4];
+            // kappa(2s + kk, lr) = 32s + 8(lr/4) + 4kk + lr%4 of the 4 rows of its group. The output tile
+            // offset (row j, columns 16cw + 4lg .. +3 of the value half) follows the V tile's swizzle.
+            int q_off[4], tr_off[4], v_off, o_off, clane, clg;
+            // Every lane-dependent value of the consumer, from lane index ln. Called again after the steady-state
+            // loop with a freshly derived lane index, so that nothing computed before the loop for use after it
+            // has to stay in a register through the loop.
+            auto lane_setup = [&](int ln) {
+                const int llr = ln & 15, llg = ln >> 4;
+                clane = ln;
+                clg = llg;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                q_off[s] = q_seg_off(lr, 4 * s + lg);
-                tr_off[s] = k_seg_off(4 * lg + (lr >> 2), 4 * s + (lr & 3));
-            }
-            const int v_off = v_seg_off(lr, 2 * cw + (lg >> 1)) + 8 * (lg & 1);
+                for (int x = 0; x < 16; ++x) fvd64[x] = lam_pow(l2, 63 - (16 * (x >> 2) + 4 * llg + (x & 3)));
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) finter[jt] = p.scale * lam_pow(l2, 16 * jt + llr + 1);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ident[e] = (4 * llg + e == llr) ? (short)0x3F80 : (short)0;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    q_off[s] = q_seg_off(llr, 4 * s + llg);
+                    tr_off[s] = k_seg_off(4 * llg + (llr >> 2), 4 * s + (llr & 3));
+                }
+                v_off = v_seg_off(llr, 2 * cw + (llg >> 1)) + 8 * (llg & 1);
+                o_off = v_off;
+            };
+            lane_setup(lane);
 
             // Carried from the iteration that takes chunk c's history term to the one that writes its output:
             // the history term (acc) and chunk c's V^T fragments (vf).
@@ -406,17 +427,22 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                 for (int it = 0; it < 4; ++it)
 #pragma unroll
                     for (int r2 = 0; r2 < 4; ++r2) {
-                        const int i = 16 * it + 4 * lg + r2;
+                        const int i = 16 * it + 4 * clg + r2;
                         fvd[4 * it + r2] = (i < lc) ? lam_pow(l2, lc - 1 - i) : 0.f;
                     }
             };
             // V fragments from the 8 raw bytes `a` of token tile it: V^T (exact, through the identity MFMA)
             // and V_dec = lambda^{lc-1-i} v_i as bf16 hi + lo
-            auto prep_part = [&](u32x2 a, int it, const float (&fvd)[16], u32x4 (&vdh)[2], u32x4 (&vdl)[2]) {
+            // (tail: the factors of a short last chunk in fvd; else the full-chunk factors fvd64)
+            auto prep_part = [&](u32x2 a, int it, bool tail, const float (&fvd)[16], u32x4 (&vdh)[2],
+                                 u32x4 (&vdl)[2]) {
                 const f32x4 x = mfma16(a, ident, f32x4{0.f, 0.f, 0.f, 0.f});
                 const uint32_t x0 = pack_bf16x2(x[0], x[1]), x1 = pack_bf16x2(x[2], x[3]);
-                const u32x2 d01 = split_bf16x2(x[0] * fvd[4 * it + 0], x[1] * fvd[4 * it + 1]);
-                const u32x2 d23 = split_bf16x2(x[2] * fvd[4 * it + 2], x[3] * fvd[4 * it + 3]);
+                float f[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) f[r] = x[r] * (tail ? fvd[4 * it + r] : fvd64[4 * it + r]);
+                const u32x2 d01 = split_bf16x2(f[0], f[1]);
+                const u32x2 d23 = split_bf16x2(f[2], f[3]);
                 if ((it & 1) == 0) {
                     vf[it >> 1].x = x0; vf[it >> 1].y = x1;
                     vdh[it >> 1].x = d01.x; vdh[it >> 1].y = d23.x;
@@ -491,13 +517,12 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                     }
             };
             auto load_p = [&](int c, u32x4 (&pf)[12]) {
-                const uint8_t *pbuf = smem + kOffP + (c & 1) * kPBufB + lane * 16;
+                const uint8_t *pbuf = smem + kOffP + (c & 1) * kPBufB + clane * 16;
 #pragma unroll
                 for (int x = 0; x < 12; ++x) pf[x] = ld16(pbuf + x * kFragB);
             };
             // chunk c's output: O = scale lambda^{j+1} history + P.V (P carries scale), rounded to bf16 into the
             // LDS output tile (row j, columns 16cw + 4lg .. +3 of the value half). Clears acc for the next chunk.
-            const int o_off = v_seg_off(lr, 2 * cw + (lg >> 1)) + 8 * (lg & 1);
             auto output = [&](int c, const u32x4 (&pf)[12]) {
                 uint8_t *ot = smem + kOffO + (c & 1) * kOTileB + o_off;
 #pragma unroll
@@ -527,9 +552,6 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                     const int lc = min(kC, len - c * kC);
                     tail_factors(lc, fvd);
                     dec = lam_pow(l2, lc);
-                } else {
-#pragma unroll
-                    for (int x = 0; x < 16; ++x) fvd[x] = fvd64[x];
                 }
                 int qb[4], kb[4];
                 bases(c, qb, kb);
@@ -548,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                     if (s < 3) load_qk(qb, kb, s + 1, qf2, kf2);
                     if (s == 0) {
 #pragma unroll
-                        for (int it = 0; it < 4; ++it) prep_part(va[it], it, fvd, vdh, vdl);
+                        for (int it = 0; it < 4; ++it) prep_part(va[it], it, tail, fvd, vdh, vdl);
                     }
                     group_mfma(s, shi, slo, qf, kf, vdh, vdl);
                     if (s < 3) {
@@ -577,6 +599,11 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
                     iteration(c, K_steady{});
                     __syncthreads();
                 }
+                {
+                    int ln = tid;
+                    asm volatile("" : "+v"(ln));
+                    lane_setup(ln & 63);
+                }
                 if (nch >= 2) {
                     iteration(nch - 1, K_last{});
                     __syncthreads();
@@ -592,7 +619,8 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params p) {
             if (s_out) {
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt)
-                    *reinterpret_cast<f32x4 *>(s_out + vrow * kD + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1)) = S[kt];
+                    *reinterpret_cast<f32x4 *>(s_out + (v0 + 16 * cw + (clane & 15)) * kD + 32 * (kt >> 1) + 8 * clg +
+                                               4 * (kt & 1)) = S[kt];
             }
         } else {
             // ======================================== producer: staging and scores / P
