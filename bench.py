@@ -7,14 +7,25 @@ timed region. Prints one JSON line. --config 0/2/3 time the other prefill worklo
 verify + commit chain through the KV buffer (B=128 requests, T=8); --config 5 times the segmented prefill of one
 long prompt (B=1, T=32768, H=HV=16) and reports the unsegmented time beside it.
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--config {0,1,2,3,4,5}]
+Timing protocol: the parent process never touches the GPU. It runs --procs fresh child processes one after the
+other (default 3); each child builds the inputs, runs the kernel for --prewarm-s seconds so that the clock has
+settled, W warmup steps, then K timed steps between HIP events on the launch stream, then K more steps with
+events around every launch (the per-launch kernel durations). The line reports the median over the children
+and the spread between them. The parent samples amd-smi clock, power and temperature every quarter second meanwhile
+and reports, per child, the samples taken from late in its pre-warm to the end of its timed launches. --procs 1 measures
+in-process, without amd-smi samples (for runs under rocprofv3).
+
+  python bench.py [--steps K] [--warmup W] [--procs N] [--no-cpu-baseline] [--config {0,1,2,3,4,5}]
+  python bench.py --trace-summary DIR/kernel_trace.csv --kernel NAME --skip S --count K   (no GPU)
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -55,19 +66,24 @@ def algorithmic_bytes(w):
     return qk + vo + nstate
 
 
+# MFMA instructions the chunked kernel issues per workgroup and 64-token chunk (one workgroup = one
+# (sequence, value head, value half) unit). Producers: 10 lower-triangle 16x16 score tiles x 4 slices of the
+# 128-wide contraction = 40 of 16x16x32. Each of the 4 consumers: history term Q S^T 4 key groups x 4 row tiles x
+# (hi, lo) = 32, state update 4 key groups x 2 tiles x 2 token pairs x (hi, lo) = 32, P.V 12, all 16x16x32; and 4
+# identity 16x16x16 transposes of its V tile. SQ_INSTS_MFMA of a config-1 launch reads 360 per workgroup-chunk.
+MFMA_X32_PER_WG_CHUNK = 40 + 4 * (32 + 32 + 12)      # 344 v_mfma_f32_16x16x32_bf16
+MFMA_X16_PER_WG_CHUNK = 4 * 4                        # 16 v_mfma_f32_16x16x16_bf16
+FLOP_X32 = 2 * 16 * 16 * 32
+FLOP_X16 = 2 * 16 * 16 * 16
+
+
 def mfma_flops_executed(w):
-    """Dense bf16 MFMA flops the kernel issues per call: per 64-token chunk and value head, scores 64x64x128 (by
-    both workgroups of a head), P.V 64x128x64 (block lower triangle, P as hi+lo), Q.S^T 64x128x128 (S as hi+lo),
-    state update 128x128x64 (V_dec as hi+lo), plus the identity transposes."""
-    per_chunk_head = (
-        2 * (10 / 16) * 64 * 64 * 128 * 2        # scores: 10 of 16 tiles, computed in each of the 2 value halves
-        + 2 * (12 / 16) * 64 * 128 * 64 * 2     # P.V: 6 of 8 32-token blocks per column tile, hi + lo
-        + 2 * 64 * 128 * 128 * 2                # Q.S^T with S hi + lo
-        + 2 * 128 * 128 * 64 * 2                # state update with V_dec hi + lo
-        + 2 * (32 + 8) * 16 * 16 * 16 * 2       # identity transposes of K (both halves) and V
-    )
+    """Dense bf16 MFMA flops the chunked kernel issues per call: the per-workgroup-chunk instruction counts above
+    times the workgroup-chunks of the call (2 value halves per (sequence, value head); a short last chunk costs a
+    whole chunk)."""
+    per_wg_chunk = MFMA_X32_PER_WG_CHUNK * FLOP_X32 + MFMA_X16_PER_WG_CHUNK * FLOP_X16
     chunks = sum((l + CHUNK - 1) // CHUNK for _, l in w.seq_rows())
-    return per_chunk_head * chunks * w.HV
+    return per_wg_chunk * chunks * w.HV * 2
 
 
 CSRC = os.path.join(ROOT, "linear_attention_decay_amd", "csrc")
@@ -112,9 +128,27 @@ def measured_traffic(config):
     return None
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def rocm_version():
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
 def cpu_baseline(w, max_units=None, min_wall_s=1.2):
     """Time the FP64 oracle on a bounded sample of the same workload: whole (sequence, value head) units."""
-    import numpy as np
     import oracle
     th = oracle.threads()
     n_units = max_units or 128
@@ -140,29 +174,117 @@ def cpu_baseline(w, max_units=None, min_wall_s=1.2):
             break
     tokheads = sum(u[1] for u in units)
     return {"value": passes * tokheads / dt / 1e6, "unit": "Mtok·head/s", "cores": th, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{len(units)} whole (sequence, value head) units of {rows[0][1]} tokens each "
                       f"({tokheads} tok·head) x {passes} passes, FP64 tokenwise recurrence, {dt:.2f} s wall "
                       f"on {th} threads"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=1, choices=range(6))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prewarm-s", type=float, default=1.0,
-                    help="untimed seconds of launches before warmup, so the timed steps run at the steady clock")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy (torch copy_) --steps times: the reference kernel that "
-                         "scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
-              f"sharding over several GPUs)", file=sys.stderr)
-        sys.exit(2)
+# ------------------------------------------------------------------------------------------------------------
+# amd-smi samples (GFX clock, socket power, hotspot temperature of GPU 0)
+# ------------------------------------------------------------------------------------------------------------
+def _walk(x):
+    if isinstance(x, dict):
+        yield x
+        for v in x.values():
+            yield from _walk(v)
+    elif isinstance(x, list):
+        for v in x:
+            yield from _walk(v)
 
+
+def _num(x):
+    if isinstance(x, dict):
+        x = x.get("value")
+    try:
+        return float(x)
+    except (TypeError, ValueError):
+        return None
+
+
+def smi_sample(timeout_s=20.0):
+    """One `amd-smi metric` reading of GPU 0: mean GFX clock over the gfx_N domains (MHz), socket power (W),
+    hotspot temperature (C). None where amd-smi is missing or reports no such field."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "-t", "--json"], capture_output=True,
+                           text=True, timeout=timeout_s)
+        data = json.loads(r.stdout)
+    except (OSError, subprocess.SubprocessError, ValueError):
+        return None
+    clocks, power, temp = [], None, None
+    for d in _walk(data):
+        for key, val in d.items():
+            if key.startswith("gfx_") and isinstance(val, dict) and "clk" in val:
+                c = _num(val["clk"])
+                if c is not None:
+                    clocks.append(c)
+            elif key == "socket_power" and power is None:
+                power = _num(val)
+            elif key == "hotspot" and temp is None:
+                temp = _num(val)
+    return {"t": round(time.time(), 2), "gfx_clock_mhz": round(sum(clocks) / len(clocks), 1) if clocks else None,
+            "socket_power_w": power, "hotspot_c": temp}
+
+
+class SmiPoller:
+    """amd-smi samples taken by the parent (which never touches the GPU) every `period` seconds, in a thread,
+    while the measurement processes run. amd-smi is itself a Python program, so it is never started from a
+    process that uses the GPU."""
+
+    def __init__(self, period=0.25):
+        self.period = period
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            s = smi_sample()
+            if s is None:
+                return
+            self.samples.append(s)
+            self._stop.wait(self.period)
+
+    def start(self):
+        self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        self._thread.join(timeout=30)
+
+    def window(self, t0, t1):
+        return [s for s in self.samples if t0 <= s["t"] <= t1]
+
+
+# ------------------------------------------------------------------------------------------------------------
+# trace summary from a rocprofv3 kernel trace (no GPU)
+# ------------------------------------------------------------------------------------------------------------
+def trace_summary(path, kernel, skip, count):
+    """Durations of the dispatches [skip, skip + count) of the kernels whose name contains `kernel`, in start
+    order, from a rocprofv3 --kernel-trace CSV; prints a markdown table row (name, dispatches in the trace,
+    selected range, average, median, min, max in ns)."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if kernel in r["Kernel_Name"]:
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort()
+    sel = rows[skip:skip + count]
+    if len(sel) < count:
+        raise SystemExit(f"{path}: {len(rows)} dispatches of {kernel}, fewer than skip {skip} + count {count}")
+    d = sorted(b - a for a, b in sel)
+    avg = sum(d) / len(d)
+    med = d[len(d) // 2] if len(d) % 2 else 0.5 * (d[len(d) // 2 - 1] + d[len(d) // 2])
+    print(f"| {kernel} | {len(rows)} | {skip} .. {skip + count - 1} | {avg:.1f} | {med:.1f} | {d[0]} | {d[-1]} |")
+    return avg
+
+
+# ------------------------------------------------------------------------------------------------------------
+# measurement in one process
+# ------------------------------------------------------------------------------------------------------------
+def measure(args):
     import numpy as np
     import torch
 
@@ -177,9 +299,7 @@ def main():
         for _ in range(args.steps):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
-                          "launches": args.steps}), flush=True)
-        return
+        return {"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": args.steps}
 
     w = la_synth.config(args.config)
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -193,11 +313,12 @@ def main():
     cu = None if w.cu_seqlens is None else to_dev(w.cu_seqlens)
     flags = w.flags
     stream = torch.cuda.current_stream(dev)
+    props = torch.cuda.get_device_properties(dev)
 
     chain = w.accepted_len is not None      # verify + commit of draft tokens through the KV buffer
     seg = args.config == 5                  # one long prompt: the segmented prefill, segment count from the CUs
     if seg:
-        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        cus = props.multi_processor_count
         n_seg = max(1, cus // (2 * w.B * w.HV))
         ws = torch.empty(max(la.la_prefill_seg_workspace_bytes(w.B, w.HV, n_seg), 4) // 4, dtype=torch.float32,
                          device=dev)
@@ -225,20 +346,25 @@ def main():
 
     # The GPU ramps its clock up over the first ~100 launches after idle; run the kernel for a fixed wall time
     # first so that the W warmup and K timed steps see the steady clock. Untimed, reported as clock_prewarm_s.
+    launches = 0
+    stamps = {"prewarm_start": time.time()}
     t_pre = time.perf_counter()
     while time.perf_counter() - t_pre < args.prewarm_s:
         for _ in range(20):
             step()
+        launches += 20
         torch.cuda.synchronize()
     prewarm_s = time.perf_counter() - t_pre
     for _ in range(args.warmup):
         step()
+    launches += args.warmup
     torch.cuda.synchronize()
 
     # timed region: K back-to-back launches on the launch stream, bracketed by events on that stream
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    stamps["timed_start"] = time.time()
     ev0.record(stream)
     for _ in range(args.steps):
         step()
@@ -256,6 +382,7 @@ def main():
     torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) for a, b in evs)
     kern_ms = sum(per) / len(per)
+    stamps["timed_end"] = time.time()
 
     plain_ms = None
     if seg:   # the same workload on the unsegmented path, for comparison
@@ -270,12 +397,86 @@ def main():
         torch.cuda.synchronize()
         plain_ms = e0.elapsed_time(e1) / args.steps
 
+    return {"ms_per_step": ms_per_step, "kernel_ms_avg": kern_ms, "kernel_ms_median": per[len(per) // 2],
+            "clock_prewarm_s": prewarm_s, "plain_ms": plain_ms, "n_seg": n_seg if seg else None,
+            # dispatch index of every kernel of the step (rocprofv3 trace order): the back-to-back timed launches,
+            # then the launches with per-launch events
+            "dispatches": {"before_timed": launches, "timed": args.steps, "per_launch_events": args.steps},
+            "gpu": {"name": props.name, "gfx_arch": getattr(props, "gcnArchName", None),
+                    "cus": props.multi_processor_count, "hip_runtime": torch.version.hip},
+            "stamps": stamps}
+
+
+def median_iqr(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return float(np.median(a)), float(np.percentile(a, 75) - np.percentile(a, 25))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1, choices=range(6))
+    ap.add_argument("--procs", type=int, default=3,
+                    help="fresh child processes to measure in (median reported); 1 = measure in this process")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-smi", action="store_true", help="skip the amd-smi clock / power samples")
+    ap.add_argument("--prewarm-s", type=float, default=1.5,
+                    help="untimed seconds of launches before warmup, so the timed steps run at the steady clock")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (torch copy_) --steps times: the reference kernel that "
+                         "scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
+    ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="summarize dispatches of --kernel from a rocprofv3 kernel trace and exit (no GPU)")
+    ap.add_argument("--kernel", default="la_chunk_kernel<0>")
+    ap.add_argument("--skip", type=int, default=0)
+    ap.add_argument("--count", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
+              f"sharding over several GPUs)", file=sys.stderr)
+        sys.exit(2)
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.kernel, args.skip, args.count)
+        return
+    if args.child or args.copy_calibration:
+        print(json.dumps(measure(args)), flush=True)
+        return
+
+    # One measurement per fresh child process; this process starts no GPU work itself.
+    runs = []
+    poller = None
+    if args.procs <= 1:
+        runs.append(measure(args))
+    else:
+        poller = None if args.no_smi else SmiPoller().start()
+        cmd = [sys.executable, os.path.abspath(__file__), "--child", "--config", str(args.config), "--steps",
+               str(args.steps), "--warmup", str(args.warmup), "--prewarm-s", str(args.prewarm_s)]
+        for i in range(args.procs):
+            r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+            if r.returncode != 0:
+                print(f"bench.py: measurement process {i} exited with status {r.returncode}", file=sys.stderr)
+                sys.exit(r.returncode if r.returncode > 0 else 1)
+            runs.append(json.loads(r.stdout.strip().splitlines()[-1]))
+        if poller is not None:
+            poller.stop()
+
+    import la_synth
+    w = la_synth.config(args.config)
+    chain = w.accepted_len is not None
+    seg = args.config == 5
+    ms_per_step, ms_iqr = median_iqr([r["ms_per_step"] for r in runs])
+    kern_ms, kern_iqr = median_iqr([r["kernel_ms_avg"] for r in runs])
     tokheads = w.tokens * w.HV
     value = tokheads / (ms_per_step * 1e-3) / 1e6
     alg_bytes = chain_bytes(w) if chain else algorithmic_bytes(w)
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     short = chain or seg or 1 <= w.T <= 16     # MFMA count below is for the plain chunked kernel only
     mfma_tfs = None if short else mfma_flops_executed(w) / (kern_ms * 1e-3) / 1e12
+    r0 = runs[0]
 
     out = {
         "metric": METRIC,
@@ -290,7 +491,6 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "clock_prewarm_s": round(prewarm_s, 3),
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "HV": w.HV, "D": 128, "DV": 128,
                    "chunk": CHUNK, "state_flags": w.flags, "tokens": w.tokens},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -298,15 +498,30 @@ def main():
                      "kernel": ("la_chunk_kernel<3> + la_seg_scan_kernel + la_chunk_kernel<4> (segmented)" if seg else
                                 "la_short_kernel<false> + la_short_kernel<true> (verify + commit)" if chain else
                                 "la_short_kernel<false>" if 1 <= w.T <= 16 else
-                                "la_chunk_kernel<1>" if cu is not None else "la_chunk_kernel<0>"),
-                     "kernel_ms_avg": round(kern_ms, 6),
-                     "kernel_ms_median": round(per[len(per) // 2], 6), "algorithmic_bytes": alg_bytes},
+                                "la_chunk_kernel<1>" if w.cu_seqlens is not None else "la_chunk_kernel<0>"),
+                     "kernel_ms_avg": round(kern_ms, 6), "algorithmic_bytes": alg_bytes},
         "mfma": None if short else {"executed_tflops": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
-                                    "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)},
+                                    "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4),
+                                    "insts_per_workgroup_chunk": {"16x16x32_bf16": MFMA_X32_PER_WG_CHUNK,
+                                                                  "16x16x16_bf16": MFMA_X16_PER_WG_CHUNK}},
+        "timing": {"processes": len(runs), "ms_per_step_each": [round(r["ms_per_step"], 6) for r in runs],
+                   "ms_per_step_iqr": round(ms_iqr, 6),
+                   "kernel_ms_avg_each": [round(r["kernel_ms_avg"], 6) for r in runs],
+                   "kernel_ms_avg_iqr": round(kern_iqr, 6),
+                   "kernel_ms_median_each": [round(r["kernel_ms_median"], 6) for r in runs],
+                   "clock_prewarm_s_each": [round(r["clock_prewarm_s"], 3) for r in runs],
+                   "dispatches_per_process": r0["dispatches"]},
+        "machine": {"gpu": r0["gpu"]["name"], "gfx_arch": r0["gpu"]["gfx_arch"], "cus": r0["gpu"]["cus"],
+                    "rocm": rocm_version(), "hip_runtime": r0["gpu"]["hip_runtime"], "cpu_model": cpu_model(),
+                    # per process: samples returned from 0.8 s into the pre-warm (amd-smi reports power and clock
+                    # averaged over its last few hundred ms) to the end of the timed launches
+                    "smi_under_load_each": None if poller is None else [
+                        poller.window(r["stamps"]["prewarm_start"] + 0.8, r["stamps"]["timed_end"]) for r in runs]},
     }
     if seg:
-        out["segmented"] = {"segments_requested": n_seg, "unsegmented_ms_per_step": round(plain_ms, 6),
-                            "speedup": round(plain_ms / ms_per_step, 3)}
+        plain, _ = median_iqr([r["plain_ms"] for r in runs])
+        out["segmented"] = {"segments_requested": r0["n_seg"], "unsegmented_ms_per_step": round(plain, 6),
+                            "speedup": round(plain / ms_per_step, 3)}
     if not args.no_cpu_baseline and args.config in (0, 1):
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
