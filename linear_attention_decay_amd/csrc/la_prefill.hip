@@ -13,7 +13,7 @@
 // Work decomposition: one workgroup = (sequence, value head, half of the 128 value columns), 8 wave64s. The 4
 // consumer waves each own value columns [16w, 16w+16) of the half: the state rows S[v][0..127] for those
 // columns stay in that wave's registers as MFMA accumulators for the whole sequence. The 4 producer waves
-// stage Q, K, V tiles into LDS two chunks ahead, compute the decay-masked intra-chunk scores and store the
+// stage Q, K, V tiles into LDS one chunk ahead, compute the decay-masked intra-chunk scores and store the
 // output tiles the consumers leave in LDS. The same kernel also runs the two chunked passes of a sequence split
 // into segments (local segment states from zero; every segment from its initial state).
 //
@@ -130,8 +130,10 @@ __device__ __forceinline__ Unit decode_unit(int u, const Params &p) {
 //   that a read of one 8-byte half of every segment allows. The tiles are filled
 //   by buffer loads that write LDS directly; the XOR is applied on the source side (lane -> segment), and
 //   rows past the end of a sequence fall outside the buffer range and arrive as zeros.
-//   Q, K, V: 3 buffers each. In the iteration that handles chunk c, both roles read chunk c's tiles, chunk
-//   c+1 has landed and chunk c+2 is in flight.
+//   Q, K, V: 2 buffers each. In the iteration that handles chunk c, both roles read chunk c's tiles while
+//   chunk c+1's loads, issued at the start of the iteration, land in the other buffers; the producers wait for
+//   them before the iteration's barrier. (One iteration covers the load latency: a third buffer, with loads two
+//   chunks ahead, measured no faster.)
 //   P: 2 buffers of 6 lower-triangle (jt, token-pair) fragment blocks, hi and lo, 64 lanes x 16 B each:
 //   written for chunk c by the producers while the consumers read chunk c-1's.
 //   O: 2 buffers of one output tile (64 rows x 128 B, bf16, swizzled like V): the consumers write chunk c-1's
@@ -142,9 +144,9 @@ constexpr int kVTileB = kC * kVW * 2;        // 8192
 constexpr int kFragB = 64 * 16;              // one fragment block
 constexpr int kPBufB = 6 * 2 * kFragB;       // 12288
 constexpr int kOffQ = 0;
-constexpr int kOffK = kOffQ + 3 * kQKTileB;
-constexpr int kOffV = kOffK + 3 * kQKTileB;
-constexpr int kOffP = kOffV + 3 * kVTileB;
+constexpr int kOffK = kOffQ + 2 * kQKTileB;
+constexpr int kOffV = kOffK + 2 * kQKTileB;
+constexpr int kOffP = kOffV + 2 * kVTileB;
 constexpr int kOTileB = kC * kVW * 2;        // 8192
 constexpr int kOffO = kOffP + 2 * kPBufB;
 constexpr int kLdsBytes = kOffO + 2 * kOTileB;
@@ -239,14 +241,12 @@ __device__ __forceinline__ void produce_scores(const float (&pf)[16], const uint
 // ---------------------------------------------------------------------------------------------------------
 // the kernel: 8 waves; waves 0..3 are consumers (state owners), waves 4..7 producers.
 //
-// Iteration c (one workgroup barrier at its end): the producers issue the staging loads of chunk c+2 and
+// Iteration c (one workgroup barrier at its end): the producers issue the staging loads of chunk c+1 and
 // compute chunk c's decay-masked scores P; the consumers finish chunk c-1's output (P of chunk c-1 from the
 // previous iteration, its history term from registers) and take chunk c's history term Q S^T and state
-// update. The producers wait only for chunk c+1's loads before the barrier, so two chunks of loads overlap
-// the compute.
+// update. The producers wait for chunk c+1's loads before the barrier, so each chunk's loads overlap one
+// iteration of compute.
 // ---------------------------------------------------------------------------------------------------------
-struct FullChunk { static constexpr bool kTail = false; };
-struct TailChunk { static constexpr bool kTail = true; };
 
 // s_waitcnt with vmcnt(N), lgkmcnt(0) and no expcnt wait (gfx9 encoding: vmcnt bits [3:0] and [15:14],
 // expcnt [6:4], lgkmcnt [11:8])
@@ -268,7 +268,6 @@ __device__ __forceinline__ void opaque_params(Params &p) {
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
     constexpr bool kOut = (MODE != kCommit && MODE != kSegStates);
-    constexpr int kStageLoads = kOut ? 10 : 6;       // buffer loads one producer wave issues per chunk
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
 
     const int tid = threadIdx.x;
@@ -454,23 +453,26 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
                 }
             };
             auto load_v = [&](int c, u32x2 (&va)[4]) {
-                const uint8_t *tv = smem + kOffV + (c % 3) * kVTileB + v_off;
+                const uint8_t *tv = smem + kOffV + (c & 1) * kVTileB + v_off;
 #pragma unroll
                 for (int it = 0; it < 4; ++it) va[it] = *reinterpret_cast<const u32x2 *>(tv + 2048 * it);
             };
             // the state before the chunk as bf16 hi + lo for the history term (key group s: keys 32s + 8lg .. +7
             // in tiles 2s, slots 0..3, and 2s+1, slots 4..7), then the decay of those two tiles
             auto split_dec = [&](int s, float dec, u32x4 &shi, u32x4 &slo) {
+                // the decayed state goes to new registers first, so that the residuals of the split can be
+                // accumulated in place into the (then dead) registers of the state before the chunk
+                const f32x4 s0 = S[2 * s], s1 = S[2 * s + 1];
+                S[2 * s] = s0 * dec;
+                S[2 * s + 1] = s1 * dec;
                 if (kOut) {
-                    const u32x2 a = split_bf16x2(S[2 * s][0], S[2 * s][1]);
-                    const u32x2 b2 = split_bf16x2(S[2 * s][2], S[2 * s][3]);
-                    const u32x2 c2 = split_bf16x2(S[2 * s + 1][0], S[2 * s + 1][1]);
-                    const u32x2 d2 = split_bf16x2(S[2 * s + 1][2], S[2 * s + 1][3]);
+                    const u32x2 a = split_bf16x2(s0[0], s0[1]);
+                    const u32x2 b2 = split_bf16x2(s0[2], s0[3]);
+                    const u32x2 c2 = split_bf16x2(s1[0], s1[1]);
+                    const u32x2 d2 = split_bf16x2(s1[2], s1[3]);
                     shi = u32x4{a.x, b2.x, c2.x, d2.x};
                     slo = u32x4{a.y, b2.y, c2.y, d2.y};
                 }
-                S[2 * s] = S[2 * s] * dec;
-                S[2 * s + 1] = S[2 * s + 1] * dec;
             };
             // Q fragments (row tiles jt = 0..3) and K^T fragments (tiles 2s, 2s+1, token pairs 0, 1) of key
             // group s; the base addresses are opaque so that the per-read constants stay in the instruction
@@ -478,8 +480,8 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
             auto bases = [&](int c, int (&qb)[4], int (&kb)[4]) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    qb[s] = kOffQ + (c % 3) * kQKTileB + q_off[s];
-                    kb[s] = kOffK + (c % 3) * kQKTileB + tr_off[s];
+                    qb[s] = kOffQ + (c & 1) * kQKTileB + q_off[s];
+                    kb[s] = kOffK + (c & 1) * kQKTileB + tr_off[s];
                     asm("" : "+v"(qb[s]), "+v"(kb[s]));
                 }
             };
@@ -646,9 +648,9 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
             auto stage = [&](int c) {
                 const int c0 = c * kC;
                 const int lc = min(kC, len - c0);
-                uint8_t *tq = smem + kOffQ + (c % 3) * kQKTileB;
-                uint8_t *tk = smem + kOffK + (c % 3) * kQKTileB;
-                uint8_t *tv = smem + kOffV + (c % 3) * kVTileB;
+                uint8_t *tq = smem + kOffQ + (c & 1) * kQKTileB;
+                uint8_t *tk = smem + kOffK + (c & 1) * kQKTileB;
+                uint8_t *tv = smem + kOffV + (c & 1) * kVTileB;
                 // buffer ranges end with the last valid row of the chunk; rows beyond read as zeros
                 const int qk_bytes = (lc - 1) * qk_stride + kD * 2;
                 const int v_bytes = (lc - 1) * v_stride + kVW * 2;
@@ -696,25 +698,18 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
                 }
             };
 
-            // Loads complete in issue order: waiting until at most one chunk's loads are outstanding means the
-            // older chunk has landed in LDS. Output stores are issued after the loads of their iteration, so
-            // they can only make such a wait stricter.
+            // Every iteration ends with all of this wave's loads and stores complete (vmcnt(0)), so the chunk
+            // staged at its start has landed in LDS before the barrier.
             if (nch > 0) stage(0);
-            if (nch > 1) {
-                stage(1);
-                wait_vmcnt_lgkm0<kStageLoads>();
-            } else {
-                wait_vmcnt_lgkm0<0>();
-            }
+            wait_vmcnt_lgkm0<0>();
             __syncthreads();
 
             for (int t = 0; t <= nch; ++t) {
-                const bool ahead = t + 2 < nch;
-                if (ahead) stage(t + 2);
+                if (t + 1 < nch) stage(t + 1);
                 if (kOut && t >= 2) store_out(t - 2);   // completed by the consumers before the last barrier
                 if (kOut && t < nch) {
-                    const uint8_t *tq = smem + kOffQ + (t % 3) * kQKTileB;
-                    const uint8_t *tk = smem + kOffK + (t % 3) * kQKTileB;
+                    const uint8_t *tq = smem + kOffQ + (t & 1) * kQKTileB;
+                    const uint8_t *tk = smem + kOffK + (t & 1) * kQKTileB;
                     uint8_t *pbuf = smem + kOffP + (t & 1) * kPBufB;
                     switch (cw) {
                     case 0: produce_scores<0, 2, 2, 1>(pf, tq, tk, pbuf, lane, lr, lg); break;
@@ -723,10 +718,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
                     default: produce_scores<0, 2, 0, 2>(pf, tq, tk, pbuf, lane, lr, lg); break;
                     }
                 }
-                if (ahead)
-                    wait_vmcnt_lgkm0<kStageLoads>();     // chunk t+1 has landed; chunk t+2 may be in flight
-                else
-                    wait_vmcnt_lgkm0<0>();
+                wait_vmcnt_lgkm0<0>();                   // chunk t+1 has landed
                 __syncthreads();
             }
             if (kOut && nch > 0) store_out(nch - 1);
