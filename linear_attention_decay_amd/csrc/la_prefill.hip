@@ -294,16 +294,19 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
 
         int64_t row0;
         int len;
+        // Values read from device memory (sequence bounds, accepted lengths, slots) are the same for every lane;
+        // readfirstlane makes that visible to the compiler, so that the buffer descriptors built from them stay
+        // in scalar registers instead of being wrapped in per-lane loops.
         if (MODE == kVarlen) {
-            int a = p.cu_seqlens[un.seq];
-            int b = p.cu_seqlens[un.seq + 1];
+            int a = __builtin_amdgcn_readfirstlane(p.cu_seqlens[un.seq]);
+            int b = __builtin_amdgcn_readfirstlane(p.cu_seqlens[un.seq + 1]);
             a = min(max(a, 0), p.total_T);
             b = min(max(b, a), p.total_T);
             row0 = a;
             len = b - a;
         } else if (MODE == kCommit) {
             row0 = (int64_t)un.seq * p.T;
-            len = min(max(p.accepted_len[un.seq], 0), p.T);
+            len = min(max(__builtin_amdgcn_readfirstlane(p.accepted_len[un.seq]), 0), p.T);
         } else if (MODE == kSegStates || MODE == kSegFwd) {
             const int per = (MODE == kSegStates) ? p.nseg - 1 : p.nseg;
             const int b = un.seq / per, g = un.seq - b * per;
@@ -331,11 +334,11 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
                 }
                 if (p.flags & (LA_STATE_READ | LA_STATE_WRITE)) {
                     int slot = -1;
-                    const int s = p.state_idx[bseq];
+                    const int s = __builtin_amdgcn_readfirstlane(p.state_idx[bseq]);
                     if (s >= 0 && s < p.pool_size) slot = s;
                     int slot_out = slot;
                     if (p.state_idx_out) {
-                        const int so = p.state_idx_out[bseq];
+                        const int so = __builtin_amdgcn_readfirstlane(p.state_idx_out[bseq]);
                         slot_out = (so >= 0 && so < p.pool_size) ? so : -1;
                     }
                     if (MODE == kCommit) {
