@@ -171,9 +171,9 @@ la_status la_prefill_fwd_varlen_ex(const void *q, const void *k, const void *v, 
                                    int32_t schedule, hipStream_t stream);
 
 /*
- * Commit after a short-chunk verify (verify page, Description: state-update advances the pooled state by the
- * per-request accepted prefix length L and skips padded slots; Tests: L = 0 is a no-op):
- *     S <- lambda^L S + sum_{i<L} lambda^{L-1-i} v_i k_i^T   over request b's first L tokens.
+ * Commit after a short-chunk verify (verify page, Description and Tests). Once the caller knows how many of
+ * request b's T draft tokens were accepted (L = accepted_len[b]), its pooled state moves past exactly those L:
+ *     S <- lambda^L S + sum_{i<L} lambda^{L-1-i} v_i k_i^T
  *   k           : bf16 [B, T, H, 128];  v : bf16 [B, T, HV, 128]
  *   state_idx   : int32 [B] (device); slot < 0 or >= pool_size: request skipped
  *   accepted_len: int32 [B] (device), 0 <= L <= T (clamped into that range on the device)
@@ -185,9 +185,9 @@ la_status la_state_commit(const void *k, const void *v, int32_t B, int32_t T, in
                           const int32_t *state_idx, const int32_t *accepted_len, hipStream_t stream);
 
 /*
- * Fused multi-token decode (verify page, Description: fused MTP decode advances the recurrence over all T draft
- * tokens per request and head in one launch): the outputs of all T tokens, and the state after them stored
- * back into each request's slot, i.e. la_prefill_fwd with flags = LA_STATE_READ | LA_STATE_WRITE.
+ * Fused multi-token decode (verify page, Description). One launch runs every (request, head) through its T draft
+ * tokens: it returns each token's output and stores the state reached after the last token back into the
+ * request's slot, i.e. la_prefill_fwd with flags = LA_STATE_READ | LA_STATE_WRITE.
  *   q, k        : bf16 [B, T, H, 128];  v, o : bf16 [B, T, HV, 128];  state_idx : int32 [B] (device)
  *   state_pool, state_idx must be non-NULL. 1 <= T <= 16 runs in one pass; longer T are chunked.
  */
@@ -196,9 +196,10 @@ la_status la_decode_mtp(const void *q, const void *k, const void *v, void *o, in
                         int32_t pool_size, const int32_t *state_idx, hipStream_t stream);
 
 /*
- * Parallel verify with a KV buffer (verify page, Description: verify computes every draft step's output in
- * closed form from the initial state without materialising intermediate states, and optionally writes k/v into
- * a compact pooled KV buffer). Outputs as la_prefill_fwd with flags = LA_STATE_READ (the pool is only read).
+ * Parallel verify with a KV buffer (verify page, Description). Each draft token's output is evaluated from the
+ * request's starting state by the closed-form sum over the draft prefix, so the state after an intermediate
+ * token never exists; the draft k and v rows can be kept on the side for a later commit. Outputs as
+ * la_prefill_fwd with flags = LA_STATE_READ (the pool is only read).
  * For every request b whose slot s = state_idx[b] is valid, the T draft rows of k and v are also copied to
  *   k_buf : bf16 [pool_size, T, H, 128]   rows k_buf[s, t]      v_buf : bf16 [pool_size, T, HV, 128]
  * so that la_state_commit_kvbuffer can advance the state later without the caller keeping k and v. Buffer
@@ -211,10 +212,10 @@ la_status la_verify_kvbuffer(const void *q, const void *k, const void *v, void *
                              void *v_buf, hipStream_t stream);
 
 /*
- * Commit from the KV buffer (verify page, Description: state-update advances the pooled state by the per-request
- * accepted prefix length L read from the buffer; padded slots are skipped; Tests: L = 0 is a no-op): as
- * la_state_commit, with request b's token rows taken from k_buf[state_idx[b], 0 .. L-1] and
- * v_buf[state_idx[b], 0 .. L-1] (layouts as written by la_verify_kvbuffer with the same T). T <= 16.
+ * Commit from the KV buffer (verify page, Description and Tests): la_state_commit with the token rows read back
+ * from the buffer la_verify_kvbuffer filled, so the caller need not keep k and v. Request b's rows are
+ * k_buf[state_idx[b], 0 .. L-1] and v_buf[state_idx[b], 0 .. L-1] (layouts as written by la_verify_kvbuffer with
+ * the same T). Out-of-range slots and L == 0 behave as in la_state_commit. T <= 16.
  */
 la_status la_state_commit_kvbuffer(const void *k_buf, const void *v_buf, int32_t B, int32_t T, int32_t H, int32_t HV,
                                    int32_t D, int32_t DV, const float *slope, float *state_pool, int32_t pool_size,

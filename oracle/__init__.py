@@ -5,14 +5,12 @@ the smoke check and the benchmark's CPU-baseline leg may import this package. It
 library and never imports it.
 
 Sources (the pages are cited by title):
-  * "[LA] Lightning Attention MTP decode + KVBuffer parallel verify / commit" -- Description, the closed form
-    used by verify: o_t = a^{t+1} (h0 q_t scale) + sum_{i<=t} a^{t-i} (q_t . k_i scale) v_i; the commit
-    advances the pooled state by a per-request accepted length L, skips negative slots, and L = 0 is a no-op
-    (Tests section).
-  * "[Lightning Attention] Add Hopper SM90 CuTe DSL prefill" -- Description (BF16 Q/K/V/O, FP32 decay and
-    state, D = V = 128, chunk 64, optional initial/final state, MHA and GVA, explicit state-pool indices, packed
-    variable-length input) and Reviewer notes (state is FP32 in [V, K] orientation; the reference checks
-    recurrence direction, same-token causality, GVA mapping, continuation and pool isolation).
+  * "[LA] Lightning Attention MTP decode + KVBuffer parallel verify / commit" -- Description (the closed form
+    o_t = a^{t+1} (h0 q_t scale) + sum_{i<=t} a^{t-i} (q_t . k_i scale) v_i of a draft output, and the commit by
+    an accepted length) and Tests (the edge cases of the commit).
+  * "[Lightning Attention] Add Hopper SM90 CuTe DSL prefill" -- Description (dtypes, head sizes, chunk length,
+    state handling, head grouping, pool indices, packed input) and Reviewer notes (the state's precision and
+    orientation, and the properties its tests cover).
 
 Three independent evaluations live here:
   * ``tokenwise`` -- the recurrence S <- lambda S + v k^T, o = scale S q, token by token in FP64 (C/OpenMP,

@@ -1,5 +1,5 @@
-"""Host-side checks of the C-ABI library (no GPU): it loads, exports every declared symbol, and answers every
-problem it can see on the host with an error status before it enqueues anything (prefill page, Description)."""
+"""Host-side checks of the C-ABI library (no GPU): it loads, exports every declared symbol, and each invalid call
+returns an error status and enqueues no work (prefill page, Description)."""
 import ctypes
 import os
 import re
