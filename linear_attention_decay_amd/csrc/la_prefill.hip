@@ -633,22 +633,29 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
             const uint8_t *qseq = reinterpret_cast<const uint8_t *>(p.q + (row0 * p.H + h) * kD);
             const uint8_t *kseq = reinterpret_cast<const uint8_t *>(p.k + (row0 * p.H + h) * kD);
             const uint8_t *vseq = reinterpret_cast<const uint8_t *>(p.v + (row0 * p.HV + un.hv) * kDV + v0);
+            // Producers 2 and 3 compute 3 score tiles each, producers 0 and 1 two; each producer shares its SIMD
+            // with one state owner. Producers 0 and 1 therefore take all of the staging loads and output
+            // stores (rows 32cw .. 32cw+31 of every tile), so that the four SIMDs carry
+            // about the same work per chunk.
+            const bool io_wave = cw < 2;
+            const int hw = cw & 1;
             // per-lane source offsets of the direct-to-LDS staging loads (the same for every chunk): Q/K
-            // block b of this producer holds rows 4(4cw+b) .. +3, lane -> (row 4(4cw+b) + lane/16, physical
-            // segment lane%16); V block b holds rows 8(2cw+b) .. +7, lane -> (row + lane/8, segment lane%8)
-            int q_src[4], k_src[4], v_src[2];
+            // block b holds rows 4(8hw+b) .. +3, lane -> (row 4(8hw+b) + lane/16, physical segment lane%16);
+            // V block b holds rows 8(4hw+b) .. +7, lane -> (row + lane/8, segment lane%8)
+            int q_src[8], k_src[8], v_src[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int r = 4 * (4 * cw + b) + (lane >> 4);
+            for (int b = 0; b < 8; ++b) {
+                const int r = 4 * (8 * hw + b) + (lane >> 4);
                 q_src[b] = r * qk_stride + (((lane & 15) ^ q_swz(r)) << 4);
                 k_src[b] = r * qk_stride + (((lane & 15) ^ k_swz(r)) << 4);
             }
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int r = 8 * (2 * cw + b) + (lane >> 3);
+            for (int b = 0; b < 4; ++b) {
+                const int r = 8 * (4 * hw + b) + (lane >> 3);
                 v_src[b] = r * v_stride + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
             }
             auto stage = [&](int c) {
+                if (!io_wave) return;
                 const int c0 = c * kC;
                 const int lc = min(kC, len - c0);
                 uint8_t *tq = smem + kOffQ + (c & 1) * kQKTileB;
@@ -662,18 +669,18 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
                 const __amdgpu_buffer_rsrc_t rv =
                     __builtin_amdgcn_make_buffer_rsrc((void *)(vseq + (int64_t)c0 * v_stride), 0, v_bytes, kBufDword3);
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(tk + (4 * cw + b) * 1024), 16, k_src[b], 0, 0, 0);
+                for (int b = 0; b < 8; ++b)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(tk + (8 * hw + b) * 1024), 16, k_src[b], 0, 0, 0);
                 if (kOut) {
                     const __amdgpu_buffer_rsrc_t rq =
                         __builtin_amdgcn_make_buffer_rsrc((void *)(qseq + (int64_t)c0 * qk_stride), 0, qk_bytes, kBufDword3);
 #pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(tq + (4 * cw + b) * 1024), 16, q_src[b], 0, 0, 0);
+                    for (int b = 0; b < 8; ++b)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(tq + (8 * hw + b) * 1024), 16, q_src[b], 0, 0, 0);
                 }
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(tv + (2 * cw + b) * 1024), 16, v_src[b], 0, 0, 0);
+                for (int b = 0; b < 4; ++b)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(tv + (4 * hw + b) * 1024), 16, v_src[b], 0, 0, 0);
             };
 
             if (kOut) {
@@ -684,9 +691,10 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
                 default: score_factors<0, 2, 0, 2>(pf, l2, p.scale, lr, lg); break;
                 }
             }
-            // chunk c's output tile from LDS to HBM: producer wave cw stores rows 16cw .. 16cw+15 of the value
+            // chunk c's output tile from LDS to HBM: producer cw < 2 stores rows 32cw .. 32cw+31 of the value
             // half, 8 lanes of 16 B per 128-byte row half; rows >= lc fall outside the buffer range and are dropped
             auto store_out = [&](int c) {
+                if (!io_wave) return;
                 const int c0 = c * kC;
                 const int lc = min(kC, len - c0);
                 const uint8_t *ot = smem + kOffO + (c & 1) * kOTileB;
@@ -694,8 +702,8 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
                     (void *)(p.o + ((row0 + c0) * p.HV + un.hv) * kDV + v0), 0, (lc - 1) * v_stride + kVW * 2,
                     kBufDword3);
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int r = 16 * cw + 8 * i + (lane >> 3);
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 32 * hw + 8 * i + (lane >> 3);
                     const u32x4 x = ld16(ot + v_seg_off(r, lane & 7));
                     __builtin_amdgcn_raw_buffer_store_b128(x, ro, r * v_stride + 16 * (lane & 7), 0, 0);
                 }
