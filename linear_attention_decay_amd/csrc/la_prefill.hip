@@ -28,7 +28,8 @@
 //
 // Precision: the state update multiplies the per-token decay into V (V_dec = lambda^{Lc-1-i} v_i) in FP32
 // and feeds it as a bf16 hi + lo pair; the FP32 state enters Q S^T as a bf16 hi + lo pair; the decay-masked
-// scores P enter P.V as a bf16 hi + lo pair. Q, K, V are exact in bf16. Every exponent handed to exp2 is
+// scores P enter P.V as a bf16 hi + lo pair (the state owners take the residuals of their two splits from an
+// MFMA against minus the identity, the producers from v_dot2c). Q, K, V are exact in bf16. Every exponent handed to exp2 is
 // <= 0, so powers of lambda can only underflow. O is rounded to bf16 once, round-to-nearest-even.
 
 #include <hip/hip_runtime.h>
@@ -170,6 +171,21 @@ __device__ __forceinline__ u32x2 ld_tr(const uint8_t *p) {
     return __builtin_bit_cast(u32x2, x);
 }
 __device__ __forceinline__ int p_blk(int jt, int ip) { return jt < 2 ? jt : 2 * jt - 2 + ip; }
+
+// x = hi + lo for the 4 values a lane holds of a 16x16 accumulator tile, hi = bf16(x), lo = bf16(x - hi). The
+// residual x - hi (exact in FP32) comes from one 16x16x16 MFMA: D = x + (-I) hi, with hi as the B operand,
+// whose lane layout (lane (n, g) holds rows 4g .. 4g+3 of column n) is that of the accumulator. The state owners
+// use this instead of v_dot2c residuals: beside MFMA work on the same SIMD a v_dot2c issues about half as fast as
+// alone, while the MFMA takes its pipe for 16 cycles per 4 values.
+__device__ __forceinline__ void split4_mfma(f32x4 x, s16x4 neg_ident, uint32_t &h0, uint32_t &h1, uint32_t &l0,
+                                            uint32_t &l1) {
+    h0 = pack_bf16x2(x[0], x[1]);
+    h1 = pack_bf16x2(x[2], x[3]);
+    const f32x4 r = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(neg_ident, __builtin_bit_cast(s16x4, u32x2{h0, h1}),
+                                                              x, 0, 0, 0);
+    l0 = pack_bf16x2(r[0], r[1]);
+    l1 = pack_bf16x2(r[2], r[3]);
+}
 
 // ---------------------------------------------------------------------------------------------------------
 // Producer: scores A^T[i][j] = K_i . Q_j for the lower-triangle 16x16 tiles of the block it in
@@ -383,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
                 for (int kt = 0; kt < 8; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
             float fvd64[16];            // V_dec factors of a full chunk, lambda^{63-i} for i = 16it+4lg+r
-            s16x4 ident;
+            s16x4 ident, neg_ident;
             // per-lane LDS offsets reused by every chunk: Q fragment (row lr, segment 4s + lg; row tile jt adds
             // 4096 B); V^T source (row lr, value tile cw; token tile it adds 2048 B); K^T source of key group s:
             // lane (lg, lr) supplies token row 4lg + lr/4 (+ 32 per token pair, + 16 for slots 4..7) and the 4
@@ -403,7 +419,10 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt) finter[jt] = p.scale * lam_pow(l2, 16 * jt + llr + 1);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ident[e] = (4 * llg + e == llr) ? (short)0x3F80 : (short)0;
+                for (int e = 0; e < 4; ++e) {
+                    ident[e] = (4 * llg + e == llr) ? (short)0x3F80 : (short)0;        // 1.0
+                    neg_ident[e] = (4 * llg + e == llr) ? (short)0xBF80 : (short)0;    // -1.0
+                }
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     q_off[s] = q_seg_off(llr, 4 * s + llg);
@@ -443,8 +462,9 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
                 float f[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) f[r] = x[r] * (tail ? fvd[4 * it + r] : fvd64[4 * it + r]);
-                const u32x2 d01 = split_bf16x2(f[0], f[1]);
-                const u32x2 d23 = split_bf16x2(f[2], f[3]);
+                uint32_t h0, h1, l0, l1;
+                split4_mfma(f32x4{f[0], f[1], f[2], f[3]}, neg_ident, h0, h1, l0, l1);
+                const u32x2 d01 = u32x2{h0, l0}, d23 = u32x2{h1, l1};
                 if ((it & 1) == 0) {
                     vf[it >> 1].x = x0; vf[it >> 1].y = x1;
                     vdh[it >> 1].x = d01.x; vdh[it >> 1].y = d23.x;
@@ -469,10 +489,10 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
                 S[2 * s] = s0 * dec;
                 S[2 * s + 1] = s1 * dec;
                 if (kOut) {
-                    const u32x2 a = split_bf16x2(s0[0], s0[1]);
-                    const u32x2 b2 = split_bf16x2(s0[2], s0[3]);
-                    const u32x2 c2 = split_bf16x2(s1[0], s1[1]);
-                    const u32x2 d2 = split_bf16x2(s1[2], s1[3]);
+                    uint32_t h0, h1, l0, l1, h2, h3, l2, l3;
+                    split4_mfma(s0, neg_ident, h0, h1, l0, l1);
+                    split4_mfma(s1, neg_ident, h2, h3, l2, l3);
+                    const u32x2 a = u32x2{h0, l0}, b2 = u32x2{h1, l1}, c2 = u32x2{h2, l2}, d2 = u32x2{h3, l3};
                     shi = u32x4{a.x, b2.x, c2.x, d2.x};
                     slo = u32x4{a.y, b2.y, c2.y, d2.y};
                 }
