@@ -29,8 +29,8 @@
 // Precision: the state update multiplies the per-token decay into V (V_dec = lambda^{Lc-1-i} v_i) in FP32
 // and feeds it as a bf16 hi + lo pair; the FP32 state enters Q S^T as a bf16 hi + lo pair; the decay-masked
 // scores P enter P.V as a bf16 hi + lo pair (the state owners take the residuals of their two splits from an
-// MFMA against minus the identity, the producers from v_dot2c). Q, K, V are exact in bf16. Every exponent handed to exp2 is
-// <= 0, so powers of lambda can only underflow. O is rounded to bf16 once, round-to-nearest-even.
+// MFMA against minus the identity, the producers from v_dot2c). Q, K, V are exact in bf16. Every exponent
+// handed to exp2 is <= 0, so powers of lambda can only underflow. O is rounded to bf16 once, round-to-nearest-even.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -175,8 +175,8 @@ __device__ __forceinline__ int p_blk(int jt, int ip) { return jt < 2 ? jt : 2 * 
 // x = hi + lo for the 4 values a lane holds of a 16x16 accumulator tile, hi = bf16(x), lo = bf16(x - hi). The
 // residual x - hi (exact in FP32) comes from one 16x16x16 MFMA: D = x + (-I) hi, with hi as the B operand,
 // whose lane layout (lane (n, g) holds rows 4g .. 4g+3 of column n) is that of the accumulator. The state owners
-// use this instead of v_dot2c residuals: beside MFMA work on the same SIMD a v_dot2c issues about half as fast as
-// alone, while the MFMA takes its pipe for 16 cycles per 4 values.
+// use this instead of v_dot2c residuals: beside MFMA work on the same SIMD a v_dot2c issues at less than half its
+// rate alone, while the MFMA takes the matrix pipe for 16 cycles per 4 values.
 __device__ __forceinline__ void split4_mfma(f32x4 x, s16x4 neg_ident, uint32_t &h0, uint32_t &h1, uint32_t &l0,
                                             uint32_t &l1) {
     h0 = pack_bf16x2(x[0], x[1]);
