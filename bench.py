@@ -72,10 +72,10 @@ def algorithmic_bytes(w):
 # (sequence, value head, value half) unit). Producers: 10 lower-triangle 16x16 score tiles x 4 slices of the
 # 128-wide contraction = 40 of 16x16x32. Each of the 4 consumers: history term Q S^T 4 key groups x 4 row tiles x
 # (hi, lo) = 32, state update 4 key groups x 2 tiles x 2 token pairs x (hi, lo) = 32, P.V 12, all 16x16x32; and
-# 16x16x16: 4 identity transposes of its V tile, 8 residuals of its S split (2 tiles x 4 key groups) and 4 of its
-# V_dec split. SQ_INSTS_MFMA of a config-1 launch reads 408 per workgroup-chunk.
+# 16x16x16: 8 residuals of its S split (2 tiles x 4 key groups) and 4 of its V_dec split. SQ_INSTS_MFMA of a
+# config-1 launch reads 392 per workgroup-chunk.
 MFMA_X32_PER_WG_CHUNK = 40 + 4 * (32 + 32 + 12)      # 344 v_mfma_f32_16x16x32_bf16
-MFMA_X16_PER_WG_CHUNK = 4 * (4 + 8 + 4)              # 64 v_mfma_f32_16x16x16_bf16
+MFMA_X16_PER_WG_CHUNK = 4 * (8 + 4)                  # 48 v_mfma_f32_16x16x16_bf16
 FLOP_X32 = 2 * 16 * 16 * 32
 FLOP_X16 = 2 * 16 * 16 * 16
 

@@ -23,8 +23,7 @@
 // instruction holds, per lane, column lane % 16 and rows 4g..4g+3. Chaining works because an accumulator
 // tile [m][n] is, lane for lane, a fragment with row n and contraction index m: scores computed as
 // A^T[i][j] feed the P.V product as P[j][i] fragments; the state kept as S^T[k][v] feeds Q.S^T as S[v][k]
-// fragments. K^T fragments come from transposing LDS reads (ds_read_b64_tr_b16) and V^T fragments from one
-// 16x16x16 MFMA against the identity (exact: a single nonzero product per output).
+// fragments. K^T and V^T fragments come from transposing LDS reads (ds_read_b64_tr_b16).
 //
 // Precision: the state update multiplies the per-token decay into V (V_dec = lambda^{Lc-1-i} v_i) in FP32
 // and feeds it as a bf16 hi + lo pair; the FP32 state enters Q S^T as a bf16 hi + lo pair; the decay-masked
@@ -399,14 +398,16 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
                 for (int kt = 0; kt < 8; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
             float fvd64[16];            // V_dec factors of a full chunk, lambda^{63-i} for i = 16it+4lg+r
-            s16x4 ident, neg_ident;
+            s16x4 neg_ident;
             // per-lane LDS offsets reused by every chunk: Q fragment (row lr, segment 4s + lg; row tile jt adds
-            // 4096 B); V^T source (row lr, value tile cw; token tile it adds 2048 B); K^T source of key group s:
-            // lane (lg, lr) supplies token row 4lg + lr/4 (+ 32 per token pair, + 16 for slots 4..7) and the 4
-            // keys 32s + 8(lr%4) + 4kk .. +3; the transposing read hands lane lr of each 16-lane group key
-            // kappa(2s + kk, lr) = 32s + 8(lr/4) + 4kk + lr%4 of the 4 rows of its group. The output tile
-            // offset (row j, columns 16cw + 4lg .. +3 of the value half) follows the V tile's swizzle.
-            int q_off[4], tr_off[4], v_off, o_off, clane, clg;
+            // 4096 B); K^T source of key group s: lane (lg, lr) supplies token row 4lg + lr/4 (+ 32 per token
+            // pair, + 16 for slots 4..7) and the 4 keys 32s + 8(lr%4) + 4kk .. +3; the transposing read hands
+            // lane lr of each 16-lane group key kappa(2s + kk, lr) = 32s + 8(lr/4) + 4kk + lr%4 of the 4 rows of
+            // its group. V^T source: lane (lg, lr) supplies token row 4lg + lr/4 and the value columns
+            // 16cw + 4(lr%4) .. +3 of the value half (token tile it adds 2048 B); the transposing read hands lane
+            // lr the 4 rows of column 16cw + lr. The output tile offset (row j, columns 16cw + 4lg .. +3 of the
+            // value half) follows the V tile's swizzle.
+            int q_off[4], tr_off[4], vt_off, o_off, clane, clg;
             // Every lane-dependent value of the consumer, from lane index ln. Called again after the steady-state
             // loop with a freshly derived lane index, so that nothing computed before the loop for use after it
             // has to stay in a register through the loop.
@@ -419,17 +420,14 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt) finter[jt] = p.scale * lam_pow(l2, 16 * jt + llr + 1);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ident[e] = (4 * llg + e == llr) ? (short)0x3F80 : (short)0;        // 1.0
-                    neg_ident[e] = (4 * llg + e == llr) ? (short)0xBF80 : (short)0;    // -1.0
-                }
+                for (int e = 0; e < 4; ++e) neg_ident[e] = (4 * llg + e == llr) ? (short)0xBF80 : (short)0;   // -1.0
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     q_off[s] = q_seg_off(llr, 4 * s + llg);
                     tr_off[s] = k_seg_off(4 * llg + (llr >> 2), 4 * s + (llr & 3));
                 }
-                v_off = v_seg_off(llr, 2 * cw + (llg >> 1)) + 8 * (llg & 1);
-                o_off = v_off;
+                vt_off = v_seg_off(4 * llg + (llr >> 2), 2 * cw + ((llr & 3) >> 1)) + 8 * (llr & 1);
+                o_off = v_seg_off(llr, 2 * cw + (llg >> 1)) + 8 * (llg & 1);
             };
             lane_setup(lane);
 
@@ -452,13 +450,15 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
                         fvd[4 * it + r2] = (i < lc) ? lam_pow(l2, lc - 1 - i) : 0.f;
                     }
             };
-            // V fragments from the 8 raw bytes `a` of token tile it: V^T (exact, through the identity MFMA)
-            // and V_dec = lambda^{lc-1-i} v_i as bf16 hi + lo
+            // V fragments of token tile it from its V^T fragment `a` (bf16 rows 4lg .. 4lg+3 of column lr, as
+            // the transposing read returns them): V^T for P.V as is, and V_dec = lambda^{lc-1-i} v_i as bf16 hi + lo
             // (tail: the factors of a short last chunk in fvd; else the full-chunk factors fvd64)
             auto prep_part = [&](u32x2 a, int it, bool tail, const float (&fvd)[16], u32x4 (&vdh)[2],
                                  u32x4 (&vdl)[2]) {
-                const f32x4 x = mfma16(a, ident, f32x4{0.f, 0.f, 0.f, 0.f});
-                const uint32_t x0 = pack_bf16x2(x[0], x[1]), x1 = pack_bf16x2(x[2], x[3]);
+                // the 4 values widened exactly to FP32 (a bf16 is the upper half of its FP32 pattern)
+                const uint32_t x0 = a.x, x1 = a.y;
+                const f32x4 x = f32x4{__builtin_bit_cast(float, x0 << 16), __builtin_bit_cast(float, x0 & 0xFFFF0000u),
+                                      __builtin_bit_cast(float, x1 << 16), __builtin_bit_cast(float, x1 & 0xFFFF0000u)};
                 float f[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) f[r] = x[r] * (tail ? fvd[4 * it + r] : fvd64[4 * it + r]);
@@ -476,9 +476,9 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
                 }
             };
             auto load_v = [&](int c, u32x2 (&va)[4]) {
-                const uint8_t *tv = smem + kOffV + (c & 1) * kVTileB + v_off;
+                const uint8_t *tv = smem + kOffV + (c & 1) * kVTileB + vt_off;
 #pragma unroll
-                for (int it = 0; it < 4; ++it) va[it] = *reinterpret_cast<const u32x2 *>(tv + 2048 * it);
+                for (int it = 0; it < 4; ++it) va[it] = ld_tr(tv + 2048 * it);
             };
             // the state before the chunk as bf16 hi + lo for the history term (key group s: keys 32s + 8lg .. +7
             // in tiles 2s, slots 0..3, and 2s+1, slots 4..7), then the decay of those two tiles
