@@ -99,6 +99,8 @@ TRAFFIC = {   # workload -> (committed FETCH_SIZE / WRITE_SIZE summary, kernel s
         ("la_common.h", "la_prefill.hip")),
     4: (os.path.join(ROOT, "profiles", "la_short_kernel_verify_commit_b128_t8_h64_hbm_traffic.md"),
         ("la_common.h", "la_short.hip")),
+    5: (os.path.join(ROOT, "profiles", "la_chunk_kernel_segmented_b1_t32768_h16_hbm_traffic.md"),
+        ("la_common.h", "la_prefill.hip")),
 }
 
 
