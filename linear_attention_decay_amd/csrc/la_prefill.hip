@@ -13,9 +13,9 @@
 // Work decomposition: one workgroup = (sequence, value head, half of the 128 value columns), 8 wave64s. The 4
 // consumer waves each own value columns [16w, 16w+16) of the half: the state rows S[v][0..127] for those
 // columns stay in that wave's registers as MFMA accumulators for the whole sequence. The 4 producer waves
-// stage Q, K, V tiles into LDS one chunk ahead, compute the decay-masked intra-chunk scores and store the
-// output tiles the consumers leave in LDS. The same kernel also runs the two chunked passes of a sequence split
-// into segments (local segment states from zero; every segment from its initial state).
+// compute the decay-masked intra-chunk scores; two of them also stage Q, K, V tiles into LDS one chunk ahead
+// and store the output tiles the consumers leave in LDS. The same kernel also runs the two chunked passes of a
+// sequence split into segments (local segment states from zero; every segment from its initial state).
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16, FP32 accumulate). Every operand fragment a lane holds is
 // "row r = lane % 16, slot group g = lane / 16, 8 slots"; slots 0..3 carry contraction indices 4g..4g+3 of
