@@ -123,11 +123,12 @@ __device__ __forceinline__ Unit decode_unit(int u, const Params &p) {
 // LDS layout (one workgroup per CU; 160 KiB).
 //   Q, K tiles: 64 rows x 256 B; V tiles (one value half): 64 rows x 128 B. Row-major as in HBM, with the
 //   16-byte segments of row r stored at segment index seg XOR (r % 16) for Q, seg XOR f(r % 16) for K
-//   (f swaps the two 2-bit halves of its argument) and seg XOR ((r/2) % 8) for V. LDS serves a 16-byte read
+//   (f swaps the two 2-bit halves of its argument) and seg XOR 2((r/2) % 4) for V. LDS serves a 16-byte read
 //   as pairs of 8-lane groups and an 8-byte read as pairs of 16-lane groups, each group within one 128-byte
 //   bank half and the two groups in opposite halves: the Q pattern makes 16-row fragment reads conflict-free;
 //   the K pattern spreads the transposing reads (4 rows x 4 segments per 16 lanes) to the two-way minimum
-//   that a read of one 8-byte half of every segment allows. The tiles are filled
+//   that a read of one 8-byte half of every segment allows; the V pattern makes the transposing reads of one
+//   value tile (4 rows x 2 segments per 16 lanes) conflict-free. The tiles are filled
 //   by buffer loads that write LDS directly; the XOR is applied on the source side (lane -> segment), and
 //   rows past the end of a sequence fall outside the buffer range and arrive as zeros.
 //   Q, K, V: 2 buffers each. In the iteration that handles chunk c, both roles read chunk c's tiles while
@@ -136,7 +137,8 @@ __device__ __forceinline__ Unit decode_unit(int u, const Params &p) {
 //   chunks ahead, measured no faster.)
 //   P: 2 buffers of 6 lower-triangle (jt, token-pair) fragment blocks, hi and lo, 64 lanes x 16 B each:
 //   written for chunk c by the producers while the consumers read chunk c-1's.
-//   O: 2 buffers of one output tile (64 rows x 128 B, bf16, swizzled like V): the consumers write chunk c-1's
+//   O: 2 buffers of one output tile (64 rows x 128 B, bf16, segments at seg XOR ((r/2) % 8), which spreads the
+//   consumers' 8-byte row writes of 16 rows over the banks): the consumers write chunk c-1's
 //   output in iteration c; the producers store it to HBM in iteration c+1 as whole 128-byte row halves.
 // ---------------------------------------------------------------------------------------------------------
 constexpr int kQKTileB = kC * kD * 2;        // 16384
@@ -159,7 +161,12 @@ __device__ __forceinline__ int q_swz(int r) { return r & 15; }
 __device__ __forceinline__ int k_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int q_seg_off(int r, int seg) { return r * 256 + ((seg ^ q_swz(r)) << 4); }
 __device__ __forceinline__ int k_seg_off(int r, int seg) { return r * 256 + ((seg ^ k_swz(r)) << 4); }
+// output tile
 __device__ __forceinline__ int v_seg_off(int r, int seg) { return r * 128 + ((seg ^ ((r >> 1) & 7)) << 4); }
+// V tile: rows 4g .. 4g+3 of a transposing read fall in alternate bank halves; the XOR 2((r/2) % 4) puts the
+// 32 bytes that rows 4g and 4g+2 (and 4g+1, 4g+3) give one value tile into different banks
+__device__ __forceinline__ int vt_swz(int r) { return ((r >> 1) & 3) << 1; }
+__device__ __forceinline__ int vt_seg_off(int r, int seg) { return r * 128 + ((seg ^ vt_swz(r)) << 4); }
 
 // 8 consecutive elements of a Q or K row: columns 8*seg .. 8*seg+7 (16-byte read)
 __device__ __forceinline__ u32x4 ld16(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
@@ -406,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
             // its group. V^T source: lane (lg, lr) supplies token row 4lg + lr/4 and the value columns
             // 16cw + 4(lr%4) .. +3 of the value half (token tile it adds 2048 B); the transposing read hands lane
             // lr the 4 rows of column 16cw + lr. The output tile offset (row j, columns 16cw + 4lg .. +3 of the
-            // value half) follows the V tile's swizzle.
+            // value half) follows the output tile's swizzle.
             int q_off[4], tr_off[4], vt_off, o_off, clane, clg;
             // Every lane-dependent value of the consumer, from lane index ln. Called again after the steady-state
             // loop with a freshly derived lane index, so that nothing computed before the loop for use after it
@@ -426,7 +433,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
                     q_off[s] = q_seg_off(llr, 4 * s + llg);
                     tr_off[s] = k_seg_off(4 * llg + (llr >> 2), 4 * s + (llr & 3));
                 }
-                vt_off = v_seg_off(4 * llg + (llr >> 2), 2 * cw + ((llr & 3) >> 1)) + 8 * (llr & 1);
+                vt_off = vt_seg_off(4 * llg + (llr >> 2), 2 * cw + ((llr & 3) >> 1)) + 8 * (llr & 1);
                 o_off = v_seg_off(llr, 2 * cw + (llg >> 1)) + 8 * (llg & 1);
             };
             lane_setup(lane);
@@ -672,7 +679,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_kernel(Params params) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 const int r = 8 * (4 * hw + b) + (lane >> 3);
-                v_src[b] = r * v_stride + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+                v_src[b] = r * v_stride + (((lane & 7) ^ vt_swz(r)) << 4);
             }
             auto stage = [&](int c) {
                 if (!io_wave) return;
