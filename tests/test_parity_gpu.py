@@ -23,7 +23,7 @@ def _log(msg):
 
 # ------------------------------------------------------------------------------------------------ small sweeps
 @pytest.mark.parametrize("G", [1, 2, 4])
-@pytest.mark.parametrize("T", [1, 7, 8, 63, 64, 65, 127, 129, 200])
+@pytest.mark.parametrize("T", [1, 7, 8, 31, 32, 33, 63, 64, 65, 97, 127, 129, 200])
 def test_fixed_sweep(T, G):
     H = 2
     w = la_synth.fixed(100 + T * 7 + G, 2, T, H, H * G, pool_slots=3, state_idx=[2, 0], flags=3, scale=0.7)
@@ -90,7 +90,7 @@ def test_extreme_decay():
 
 
 def test_varlen_small_with_edges():
-    lengths = [0, 1, 64, 65, 7, 128, 200, 0, 63]
+    lengths = [0, 1, 64, 65, 7, 128, 200, 0, 63, 32, 33]
     w = la_synth.varlen(21, len(lengths), 0, 2, 4, pool_slots=12, n_skip=2, flags=3, lengths=lengths, scale=0.9)
     w.state_idx[3] = 40          # >= pool size: treated as "no state"
     d = DevWorkload(w)
